@@ -1,0 +1,165 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) fused top-k Mixture-of-Experts layer.
+ *
+ * The layer, as the pages describe it: a router yields a weight
+ * distribution over E experts, each token keeps its top-k experts, the
+ * tokens are sorted by expert so every expert's rows are contiguous, one
+ * grouped kernel multiplies each slice by its own expert's weights, and
+ * the expert outputs are summed back in token order with the routing
+ * weights (FusedMoE vs MegaMoE post, sections 2 and 3.1).  Each expert
+ * product is A[M,K] x B[K,N] over the expert's routed token rows (MoE
+ * kernel engineering post, Eq. 1); weights are stored as the K-contiguous
+ * transpose B^T[N,K] that the Swap-AB formulation puts in the leading
+ * operand (same post, Eq. 2).
+ *
+ * Conventions for every call:
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device and be 16-byte aligned.  The library never
+ *    allocates, frees or keeps a pointer after a call returns.
+ *  - Every call enqueues work on `stream` (a hipStream_t passed as void*;
+ *    NULL is the null stream) and returns without synchronising.  Device
+ *    faults surface at the caller's next synchronisation.
+ *  - Arguments are validated on the host before any HIP call; a rejected
+ *    call enqueues nothing.  M = 0 is a valid no-op.
+ *  - Matrices are row-major.  Outputs are overwritten, never accumulated.
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    MOE_ERR_SHAPE = 2,       /* M<0, E<1, topk<1, topk>E, H or I not a multiple of 128, ... */
+    MOE_ERR_UNSUPPORTED = 3, /* E>256, topk>16, dtype/kind combination, block_m      */
+    MOE_ERR_WORKSPACE = 4,   /* workspace smaller than fused_moe_workspace_size()   */
+    MOE_ERR_ALIGNMENT = 5,   /* a pointer is not 16-byte aligned                    */
+    MOE_ERR_HIP = 6          /* a HIP launch failed                                 */
+} moe_status;
+
+typedef enum {
+    MOE_F32 = 0,     /* IEEE binary32                                          */
+    MOE_BF16 = 1,    /* bfloat16                                               */
+    MOE_FP8_E4M3 = 2 /* OCP OFP8 E4M3 (bias 7, max 448, no inf) + float32 scale */
+} moe_dtype;
+
+typedef enum {
+    MOE_GEMM_GATE_UP_SILU = 0, /* act[p] = silu(W1[e][0:I] x) * (W1[e][I:2I] x) */
+    MOE_GEMM_DOWN = 1          /* y[p]   = W2[e] act[p]                         */
+} moe_gemm_kind;
+
+/* The index system produced by moe_align (all device pointers, int32):
+ *  sorted_ids[cap]        pair ids p = t*topk + j grouped by expert, stable in p;
+ *                         every expert's run is padded to a multiple of block_m
+ *                         with the sentinel P = M*topk, and rows past the padded
+ *                         total hold P as well
+ *  tile_expert[cap/block_m]  expert of each block_m-row tile, -1 past the total
+ *  expert_counts[E]       pairs routed to each expert
+ *  expert_offsets[E+1]    exclusive prefix sum of the padded counts; the last
+ *                         entry is the padded total
+ *  active_experts[min(E,P)]  experts with a non-zero count, ascending, then -1
+ *  num_active[1]          number of experts with a non-zero count
+ * where cap = moe_align_capacity(M, topk, E, block_m). */
+typedef struct {
+    int32_t* sorted_ids;
+    int32_t* tile_expert;
+    int32_t* expert_counts;
+    int32_t* expert_offsets;
+    int32_t* active_experts;
+    int32_t* num_active;
+} moe_align_bufs;
+
+/* Top-k routing (FusedMoE vs MegaMoE post, section 2; section 3.1 step 1).
+ *  logits        device, float32 [M][E], finite (non-finite values give
+ *                unspecified ids, but every id written is in [0, E))
+ *  topk_ids      device, int32 [M][topk]: slot j holds the j-th largest logit,
+ *                ties broken by the lower expert index (+0 and -0 are equal)
+ *  topk_weights  device, float32 [M][topk]: exp(l_j - l_max) divided by the
+ *                sum over the selected experts (renormalize != 0) or over all
+ *                E experts (renormalize == 0)
+ * Errors: NULL -> MOE_ERR_NULL; M<0, E<1, topk<1, topk>E -> MOE_ERR_SHAPE;
+ * E>256 or topk>16 -> MOE_ERR_UNSUPPORTED. */
+moe_status moe_route(const float* logits, int32_t M, int32_t E, int32_t topk, int32_t renormalize,
+                     int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* Rows of sorted_ids needed by moe_align: the smallest multiple of block_m
+ * that is >= P + min(E, P) * (block_m - 1), P = M*topk.  Pure host function;
+ * returns -1 for invalid arguments. */
+int64_t moe_align_capacity(int32_t M, int32_t topk, int32_t E, int32_t block_m);
+
+/* Token-to-expert alignment (FusedMoE vs MegaMoE post, section 3.1 steps 1-2):
+ * per-expert counts, padded exclusive prefix sum, stable sort of the pairs
+ * by expert, tile->expert map and the compacted active-expert list.  Output
+ * is fully determined by topk_ids (no dependence on scheduling).
+ *  topk_ids  device, int32 [M][topk], each in [0, E) (ids outside are skipped)
+ *  out       device buffers sized as described at moe_align_bufs
+ * block_m must be one of 1, 16, 32, 64, 128, 256 (else MOE_ERR_UNSUPPORTED). */
+moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t E, int32_t block_m,
+                     moe_align_bufs out, void* stream);
+
+/* Grouped expert GEMM over routed rows (section 3.1 step 3; Eq. 1 per
+ * expert, with the weights in the leading operand at decode per Eq. 2).
+ *  kind = MOE_GEMM_GATE_UP_SILU: a = x [M][K=H], w = W1 [E][N=2I][K] (gate rows
+ *         0..I-1, up rows I..2I-1), c = act [P][I] in pair order.
+ *  kind = MOE_GEMM_DOWN: a = act [P][K=I], w = W2 [E][N=H][K], c = y [P][N] in
+ *         pair order.
+ *  dtype: MOE_F32 (a, w, c float32), MOE_BF16 (a, w, c bfloat16),
+ *         MOE_FP8_E4M3 (w e4m3 with w_scale[E] float32 per expert matrix;
+ *         GATE_UP: a = x e4m3 with a_scale -> its float32 scale, c = act
+ *         bfloat16, c_amax -> float32 that receives max|act| (zeroed by the
+ *         call itself); DOWN: a = act bfloat16, a_scale -> that amax, the act
+ *         rows are quantised on load with s = amax/448, c = y bfloat16).
+ *  a_scale, w_scale, c_amax must be NULL unless dtype is MOE_FP8_E4M3.
+ *  al, block_m: the output of moe_align for the same topk_ids and block_m.
+ *  Rows of a expert's run are read through al->sorted_ids; only the first
+ *  expert_counts[e] rows of each run are written to c.
+ * Errors as for the other calls; K and N must be multiples of 128. */
+moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, const float* a_scale,
+                            const void* w, const float* w_scale, const moe_align_bufs* al, int32_t M,
+                            int32_t topk, int32_t E, int32_t N, int32_t K, int32_t block_m, void* c,
+                            float* c_amax, void* stream);
+
+/* Weighted combine back into token order (section 3.1 step 4):
+ *  out[t][h] = sum_{j=0..topk-1} topk_weights[t][j] * y[t*topk+j][h], j
+ *  ascending, float32 accumulation.
+ *  y_dtype: MOE_F32 or MOE_BF16; out_dtype: MOE_F32 or MOE_BF16.
+ *  y device [M*topk][H]; topk_weights device [M][topk]; out device [M][H]. */
+moe_status moe_combine(moe_dtype y_dtype, const void* y, const float* topk_weights, int32_t M,
+                       int32_t topk, int32_t H, moe_dtype out_dtype, void* out, void* stream);
+
+/* Bytes of device workspace fused_moe needs for these sizes (0 for M=0). */
+size_t fused_moe_workspace_size(moe_dtype dtype, int32_t M, int32_t E, int32_t topk, int32_t H,
+                                int32_t I);
+
+/* The whole layer: route -> align -> GATE_UP GEMM -> DOWN GEMM -> combine, all
+ * on `stream`, no host synchronisation.
+ *  x              device [M][H]: float32, bfloat16 or e4m3 (x_scale -> float32)
+ *  router_logits  device float32 [M][E]
+ *  w1, w2         device [E][2I][H] and [E][H][I] in dtype (fp8: w1_scale,
+ *                 w2_scale device float32 [E])
+ *  out            device [M][H]: float32 for MOE_F32, bfloat16 otherwise
+ *  topk_ids_out, topk_weights_out  optional device [M][topk] copies of the
+ *                 routing result (NULL to skip)
+ *  workspace      device, >= fused_moe_workspace_size(...) bytes, 256-byte
+ *                 aligned; its contents on entry do not matter. */
+moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
+                     const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
+                     int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize,
+                     void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_str(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,557 @@
+// Grouped expert GEMMs over routed rows (FusedMoE vs MegaMoE post, section
+// 3.1 step 3: one kernel multiplies every expert's sorted slice by that
+// expert's weights).  Two kernel families:
+//
+//  decode   - few rows per expert.  Weight rows sit on the MFMA row
+//             operand (16 rows) and the expert's tokens on the 16-wide
+//             column operand, so C^T[N,M] = B^T[N,K] A^T[K,M] (MoE kernel
+//             engineering post, Eq. 2, the Swap-AB formulation).  Each
+//             workgroup owns 64 weight rows of one active expert and
+//             streams them from HBM exactly once per pass over the expert's
+//             tokens; its four wavefronts split K and reduce through LDS.
+//  prefill  - many rows per expert.  Tokens on the row operand, weights on
+//             the column operand (Eq. 1), BM x 128 output tiles staged
+//             through LDS, one tile of block_m sorted rows per workgroup row.
+//
+// Both use v_mfma_f32_16x16x32_{bf16,fp8_fp8}.  Within one instruction the
+// pairing of k indices between the two operands is the same for A and B,
+// so any permutation of K applied identically to both operands leaves the
+// dot product unchanged; the loaders use that to give each lane 64
+// contiguous bytes of a row.
+#include <stdlib.h>
+#include <string.h>
+
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+// ------------------------------------------------------------- operands
+
+template <int DT>
+struct Opnd;
+
+template <>
+struct Opnd<MOE_BF16> {
+    using chunk = uint4;  // 8 bf16
+    static constexpr int kElemBytes = 2;
+    __device__ static __forceinline__ f32x4 mfma(const chunk& a, const chunk& b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Opnd<MOE_FP8_E4M3> {
+    using chunk = uint2;  // 8 e4m3
+    static constexpr int kElemBytes = 1;
+    __device__ static __forceinline__ f32x4 mfma(const chunk& a, const chunk& b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a),
+                                                          __builtin_bit_cast(long, b), c, 0, 0, 0);
+    }
+};
+
+// 8 bf16 activations quantised to 8 e4m3 codes with value/s (IEEE division).
+__device__ __forceinline__ uint2 quant8(const uint4& v, float s) {
+    float f[8];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16) / s;
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) / s;
+    }
+    uint2 r;
+    r.x = pack_fp8x4(f[0], f[1], f[2], f[3]);
+    r.y = pack_fp8x4(f[4], f[5], f[6], f[7]);
+    return r;
+}
+
+__device__ __forceinline__ float act_scale_from_amax(const float* amax) {
+    float a = *amax;
+    return a > 0.0f ? a / 448.0f : 1.0f;
+}
+
+struct GemmArgs {
+    const void* a;
+    const float* a_scale;
+    const void* w;
+    const float* w_scale;
+    const int32_t* sorted;
+    const int32_t* tile_expert;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* active;
+    const int32_t* num_active;
+    int topk, N, K, P;
+    void* c;
+    float* c_amax;
+};
+
+__device__ __forceinline__ void amax_publish(float m, float* dst) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (__lane_id() == 0 && m > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(dst), __float_as_uint(m));
+}
+
+// ----------------------------------------------------------------- decode
+
+constexpr int kDecThreads = 256;
+constexpr int kDecU = 4;  // MFMAs per row tile per K step: each lane holds 32 consecutive elements
+
+template <int KIND, int DT, int NT>
+__global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
+    using O = Opnd<DT>;
+    using chunk = typename O::chunk;
+    constexpr int kElem = O::kElemBytes;
+    constexpr int kStep = 128;  // K elements per step (4 lane groups x 32)
+
+    const int slot = blockIdx.y;
+    if (slot >= *g.num_active) return;
+    const int e = g.active[slot];
+    const int cnt = g.counts[e];
+    const int base = g.offsets[e];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int lr = lane & 15;  // row within a 16-row tile / token column
+    const int lg = lane >> 4;  // lane group: 32-element span inside a step
+    const int K = g.K, N = g.N;
+    const int I = N / 2;
+    const int nsteps = K / kStep;
+
+    // weight rows of the four 16-row tiles
+    const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 32 : blockIdx.x * 64;
+    const char* wbase = reinterpret_cast<const char*>(g.w) + (size_t)e * N * K * kElem;
+    const char* arow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int row;
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
+            row = (i < 2) ? n0 + 16 * i + lr : I + n0 + 16 * (i - 2) + lr;
+        else
+            row = n0 + 16 * i + lr;
+        arow[i] = wbase + ((size_t)row * K + lg * 32) * kElem;
+    }
+
+    float scale = 1.0f, qs = 1.0f;
+    if constexpr (DT == MOE_FP8_E4M3) {
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+            scale = g.a_scale[0] * g.w_scale[e];
+        } else {
+            qs = act_scale_from_amax(g.a_scale);
+            scale = qs * g.w_scale[e];
+        }
+    }
+
+    extern __shared__ f32x4 red[];  // [4 waves][4 tiles][NT][64 lanes]
+    float amax = 0.0f;
+
+    for (int pass = 0; pass < cnt; pass += NT * 16) {
+        const int ntiles = min(NT, (cnt - pass + 15) / 16);
+        // source rows of this lane's token columns
+        const char* brow[NT];
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            int r = min(pass + c * 16 + lr, cnt - 1);
+            int p = g.sorted[base + r];
+            if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
+                brow[c] = reinterpret_cast<const char*>(g.a) + ((size_t)(p / g.topk) * K + lg * 32) * kElem;
+            else if constexpr (DT == MOE_FP8_E4M3)
+                brow[c] = reinterpret_cast<const char*>(g.a) + ((size_t)p * K + lg * 32) * 2;  // bf16 act
+            else
+                brow[c] = reinterpret_cast<const char*>(g.a) + ((size_t)p * K + lg * 32) * kElem;
+        }
+
+        f32x4 acc[4][NT];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < NT; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int s = wave; s < nsteps; s += 4) {
+            const size_t koff = (size_t)s * kStep;
+            chunk av[4][kDecU];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int u = 0; u < kDecU; ++u)
+                    av[i][u] = *reinterpret_cast<const chunk*>(arow[i] + (koff + u * 8) * kElem);
+            chunk bv[NT][kDecU];
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                if (c < ntiles) {
+#pragma unroll
+                    for (int u = 0; u < kDecU; ++u) {
+                        if constexpr (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) {
+                            uint4 h = *reinterpret_cast<const uint4*>(brow[c] + (koff + u * 8) * 2);
+                            bv[c][u] = __builtin_bit_cast(chunk, quant8(h, qs));
+                        } else {
+                            bv[c][u] = *reinterpret_cast<const chunk*>(brow[c] + (koff + u * 8) * kElem);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                if (c < ntiles) {
+#pragma unroll
+                    for (int u = 0; u < kDecU; ++u)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[i][c] = O::mfma(av[i][u], bv[c][u], acc[i][c]);
+                }
+            }
+        }
+
+        // K-split reduction across the four wavefronts
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < NT; ++c) red[((wave * 4 + i) * NT + c) * 64 + lane] = acc[i][c];
+        __syncthreads();
+
+        const int units = (KIND == MOE_GEMM_GATE_UP_SILU) ? 2 * ntiles : 4 * ntiles;
+        for (int u = wave; u < units; u += 4) {
+            const int r = pass + (u / ((KIND == MOE_GEMM_GATE_UP_SILU) ? 2 : 4)) * 16 + lr;
+            const int c = u / ((KIND == MOE_GEMM_GATE_UP_SILU) ? 2 : 4);
+            if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+                const int q = u % 2;
+                f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    gs += red[((w * 4 + q) * NT + c) * 64 + lane];
+                    us += red[((w * 4 + q + 2) * NT + c) * 64 + lane];
+                }
+                if (r < cnt) {
+                    const int p = g.sorted[base + r];
+                    float o[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float gv = gs[v] * scale, uv = us[v] * scale;
+                        o[v] = silu(gv) * uv;
+                    }
+                    uint2 pk;
+                    pk.x = pack_bf2(o[0], o[1]);
+                    pk.y = pack_bf2(o[2], o[3]);
+                    if constexpr (DT == MOE_FP8_E4M3) {
+                        amax = fmaxf(amax, fabsf(bf2f(pk.x & 0xffff)));
+                        amax = fmaxf(amax, fabsf(bf2f(pk.x >> 16)));
+                        amax = fmaxf(amax, fabsf(bf2f(pk.y & 0xffff)));
+                        amax = fmaxf(amax, fabsf(bf2f(pk.y >> 16)));
+                    }
+                    const int n = n0 + 16 * q + 4 * lg;
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * I + n) = pk;
+                }
+            } else {
+                const int i = u % 4;
+                f32x4 ys = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) ys += red[((w * 4 + i) * NT + c) * 64 + lane];
+                if (r < cnt) {
+                    const int p = g.sorted[base + r];
+                    const int n = n0 + 16 * i + 4 * lg;
+                    uint2 pk;
+                    pk.x = pack_bf2(ys[0] * scale, ys[1] * scale);
+                    pk.y = pack_bf2(ys[2] * scale, ys[3] * scale);
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * N + n) = pk;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) amax_publish(amax, g.c_amax);
+}
+
+// ---------------------------------------------------------------- prefill
+
+constexpr int kPreThreads = 256;
+constexpr int kPreBN = 128;  // weight rows per workgroup
+constexpr int kPreBK = 64;   // K elements per stage
+
+template <int KIND, int DT, int BM>
+__global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
+    using O = Opnd<DT>;
+    using chunk = typename O::chunk;
+    constexpr int kElem = O::kElemBytes;
+    constexpr int kRowBytes = kPreBK * kElem;        // bytes of one staged row
+    constexpr int kLdsStride = kRowBytes + 16;       // padded LDS row
+    constexpr int kChunksPerRow = kRowBytes / 16;    // 16-byte global chunks per row
+    constexpr int kAChunks = BM * kChunksPerRow / kPreThreads;
+    constexpr int kBChunks = kPreBN * kChunksPerRow / kPreThreads;
+    constexpr int kWM = BM / 2;       // rows per wavefront
+    constexpr int kTM = kWM / 16;     // 16-row tiles per wavefront
+
+    const int tile = blockIdx.y;
+    const int e = g.tile_expert[tile];
+    if (e < 0) return;
+
+    __shared__ __attribute__((aligned(16))) char As[BM * kLdsStride];
+    __shared__ __attribute__((aligned(16))) char Bs[kPreBN * kLdsStride];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int K = g.K, N = g.N, I = N / 2;
+    const int P = g.P;
+
+    float qs = 1.0f, scale = 1.0f;
+    if constexpr (DT == MOE_FP8_E4M3) {
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+            scale = g.a_scale[0] * g.w_scale[e];
+        } else {
+            qs = act_scale_from_amax(g.a_scale);
+            scale = qs * g.w_scale[e];
+        }
+    }
+
+    // global sources of the chunks this thread stages
+    const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 64 : blockIdx.x * 128;
+    const char* asrc[kAChunks];
+    const char* bsrc[kBChunks];
+    int adst[kAChunks], bdst[kBChunks];
+    const bool a_is_bf16_act = (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3);
+#pragma unroll
+    for (int q = 0; q < kAChunks; ++q) {
+        int id = tid + q * kPreThreads;
+        int r = id / kChunksPerRow, cc = id % kChunksPerRow;
+        int p = g.sorted[tile * BM + r];
+        adst[q] = r * kLdsStride + cc * 16;
+        if (p >= P) {
+            asrc[q] = nullptr;
+        } else if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+            asrc[q] = reinterpret_cast<const char*>(g.a) + (size_t)(p / g.topk) * K * kElem + cc * 16;
+        } else if (a_is_bf16_act) {
+            asrc[q] = reinterpret_cast<const char*>(g.a) + (size_t)p * K * 2 + cc * 32;
+        } else {
+            asrc[q] = reinterpret_cast<const char*>(g.a) + (size_t)p * K * kElem + cc * 16;
+        }
+    }
+    const char* wbase = reinterpret_cast<const char*>(g.w) + (size_t)e * N * K * kElem;
+#pragma unroll
+    for (int q = 0; q < kBChunks; ++q) {
+        int id = tid + q * kPreThreads;
+        int j = id / kChunksPerRow, cc = id % kChunksPerRow;
+        int row = (KIND == MOE_GEMM_GATE_UP_SILU) ? ((j < 64) ? n0 + j : I + n0 + j - 64) : n0 + j;
+        bsrc[q] = wbase + (size_t)row * K * kElem + cc * 16;
+        bdst[q] = j * kLdsStride + cc * 16;
+    }
+
+    uint4 ra[kAChunks], rb[kBChunks];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < kAChunks; ++q) {
+            if (!asrc[q]) {
+                ra[q] = uint4{0, 0, 0, 0};
+            } else if (a_is_bf16_act) {
+                const uint4* s = reinterpret_cast<const uint4*>(asrc[q] + (size_t)k0 * 2);
+                uint2 lo = quant8(s[0], qs), hi = quant8(s[1], qs);
+                ra[q] = uint4{lo.x, lo.y, hi.x, hi.y};
+            } else {
+                ra[q] = *reinterpret_cast<const uint4*>(asrc[q] + (size_t)k0 * kElem);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kBChunks; ++q) rb[q] = *reinterpret_cast<const uint4*>(bsrc[q] + (size_t)k0 * kElem);
+    };
+    auto sstore = [&]() {
+#pragma unroll
+        for (int q = 0; q < kAChunks; ++q) *reinterpret_cast<uint4*>(As + adst[q]) = ra[q];
+#pragma unroll
+        for (int q = 0; q < kBChunks; ++q) *reinterpret_cast<uint4*>(Bs + bdst[q]) = rb[q];
+    };
+
+    f32x4 acc[kTM][4];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // LDS rows of this wavefront's column tiles
+    int bcol[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
+            bcol[j] = (j < 2) ? wn * 32 + 16 * j : 64 + wn * 32 + 16 * (j - 2);
+        else
+            bcol[j] = wn * 64 + 16 * j;
+    }
+
+    const int nk = K / kPreBK;
+    gload(0);
+    sstore();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk) gload((kt + 1) * kPreBK);
+#pragma unroll
+        for (int ks = 0; ks < kPreBK / 32; ++ks) {
+            const int koff = (ks * 32 + lg * 8) * kElem;
+            chunk af[kTM], bf[4];
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+                af[i] = *reinterpret_cast<const chunk*>(As + (wm * kWM + 16 * i + lr) * kLdsStride + koff);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bf[j] = *reinterpret_cast<const chunk*>(Bs + (bcol[j] + lr) * kLdsStride + koff);
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = O::mfma(af[i], bf[j], acc[i][j]);
+        }
+        __syncthreads();
+        if (kt + 1 < nk) {
+            sstore();
+            __syncthreads();
+        }
+    }
+
+    // epilogue: lane holds C[token row 4*lg+v][weight col lr] of each tile
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = wm * kWM + 16 * i + 4 * lg + v;
+            const int p = g.sorted[tile * BM + r];
+            if (p >= P) continue;
+            if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float gv = acc[i][j][v] * scale, uv = acc[i][j + 2][v] * scale;
+                    uint16_t h = f2bf(silu(gv) * uv);
+                    if constexpr (DT == MOE_FP8_E4M3) amax = fmaxf(amax, fabsf(bf2f(h)));
+                    const int n = n0 + wn * 32 + 16 * j + lr;
+                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * I + n] = h;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = n0 + wn * 64 + 16 * j + lr;
+                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * N + n] = f2bf(acc[i][j][v] * scale);
+                }
+            }
+        }
+    }
+    if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) amax_publish(amax, g.c_amax);
+}
+
+// ------------------------------------------------------------------- f32
+//
+// Plain fp32 path: one thread per (sorted row, output column), dot products
+// straight from global memory.
+
+template <int KIND>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g, int block_m, int cap) {
+    const int n = blockIdx.y * 64 + (threadIdx.x & 63);
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= cap) return;
+    const int e = g.tile_expert[r / block_m];
+    if (e < 0) return;
+    const int p = g.sorted[r];
+    if (p >= g.P) return;
+    const int K = g.K, N = g.N;
+    const float* w = reinterpret_cast<const float*>(g.w) + (size_t)e * N * K;
+    if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+        const int I = N / 2;
+        if (n >= I) return;
+        const float* x = reinterpret_cast<const float*>(g.a) + (size_t)(p / g.topk) * K;
+        float gs = 0.f, us = 0.f;
+        for (int k = 0; k < K; ++k) {
+            gs = fmaf(w[(size_t)n * K + k], x[k], gs);
+            us = fmaf(w[(size_t)(I + n) * K + k], x[k], us);
+        }
+        reinterpret_cast<float*>(g.c)[(size_t)p * I + n] = gs / (1.0f + expf(-gs)) * us;
+    } else {
+        if (n >= N) return;
+        const float* a = reinterpret_cast<const float*>(g.a) + (size_t)p * K;
+        float s = 0.f;
+        for (int k = 0; k < K; ++k) s = fmaf(w[(size_t)n * K + k], a[k], s);
+        reinterpret_cast<float*>(g.c)[(size_t)p * N + n] = s;
+    }
+}
+
+// --------------------------------------------------------------- dispatch
+
+int prefill_supported_block_m(int block_m) { return block_m == 64 || block_m == 128; }
+
+GemmPath choose_gemm_path(const GemmCall& g) {
+    const char* env = getenv("MOE_GEMM_PATH");
+    const bool pre_ok = prefill_supported_block_m(g.block_m);
+    if (env && strcmp(env, "decode") == 0) return GemmPath::kDecode;
+    if (env && strcmp(env, "prefill") == 0 && pre_ok) return GemmPath::kPrefill;
+    const long P = (long)g.M * g.topk;
+    const long per_expert = P / g.E;
+    return (per_expert > 64 && pre_ok) ? GemmPath::kPrefill : GemmPath::kDecode;
+}
+
+template <int KIND, int DT, int NT>
+static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, hipStream_t s) {
+    const int nblk = (KIND == MOE_GEMM_GATE_UP_SILU) ? (a.N / 2) / 32 : a.N / 64;
+    const size_t lds = sizeof(f32x4) * 4 * 4 * NT * 64;
+    hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT>), dim3(nblk, nslots), dim3(kDecThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int KIND, int DT>
+static hipError_t launch_decode(const GemmArgs& a, int M, int topk, int E, hipStream_t s) {
+    const long P = (long)M * topk;
+    const int nslots = (int)(P < E ? P : E);
+    const long avg = (P + E - 1) / E;
+    if (avg <= 10) return launch_decode_nt<KIND, DT, 1>(a, nslots, s);
+    if (avg <= 24) return launch_decode_nt<KIND, DT, 2>(a, nslots, s);
+    return launch_decode_nt<KIND, DT, 4>(a, nslots, s);
+}
+
+template <int KIND, int DT>
+static hipError_t launch_prefill(const GemmArgs& a, int block_m, int64_t cap, hipStream_t s) {
+    const int nblk = (KIND == MOE_GEMM_GATE_UP_SILU) ? (a.N / 2) / 64 : a.N / 128;
+    const int ntiles = (int)(cap / block_m);
+    if (block_m == 64)
+        hipLaunchKernelGGL((gemm_prefill_kernel<KIND, DT, 64>), dim3(nblk, ntiles), dim3(kPreThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_prefill_kernel<KIND, DT, 128>), dim3(nblk, ntiles), dim3(kPreThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t launch_kind(const GemmCall& c, const GemmArgs& a, int64_t cap, hipStream_t s) {
+    if (c.dtype == MOE_F32) {
+        const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? c.N / 2 : c.N;
+        dim3 grid((unsigned)((cap + 3) / 4), (ncols + 63) / 64);
+        hipLaunchKernelGGL((gemm_f32_kernel<KIND>), grid, dim3(256), 0, s, a, c.block_m, (int)cap);
+        return hipGetLastError();
+    }
+    const GemmPath path = choose_gemm_path(c);
+    if (c.dtype == MOE_BF16) {
+        if (path == GemmPath::kPrefill) return launch_prefill<KIND, MOE_BF16>(a, c.block_m, cap, s);
+        return launch_decode<KIND, MOE_BF16>(a, c.M, c.topk, c.E, s);
+    }
+    if (path == GemmPath::kPrefill) return launch_prefill<KIND, MOE_FP8_E4M3>(a, c.block_m, cap, s);
+    return launch_decode<KIND, MOE_FP8_E4M3>(a, c.M, c.topk, c.E, s);
+}
+
+hipError_t launch_grouped_gemm(const GemmCall& c, hipStream_t s) {
+    if (c.M == 0) return hipSuccess;
+    GemmArgs a;
+    a.a = c.a;
+    a.a_scale = c.a_scale;
+    a.w = c.w;
+    a.w_scale = c.w_scale;
+    a.sorted = c.al.sorted_ids;
+    a.tile_expert = c.al.tile_expert;
+    a.counts = c.al.expert_counts;
+    a.offsets = c.al.expert_offsets;
+    a.active = c.al.active_experts;
+    a.num_active = c.al.num_active;
+    a.topk = c.topk;
+    a.N = c.N;
+    a.K = c.K;
+    a.P = c.M * c.topk;
+    a.c = c.c;
+    a.c_amax = c.c_amax;
+    const int64_t cap = moe_align_capacity(c.M, c.topk, c.E, c.block_m);
+    if (c.kind == MOE_GEMM_GATE_UP_SILU) return launch_kind<MOE_GEMM_GATE_UP_SILU>(c, a, cap, s);
+    return launch_kind<MOE_GEMM_DOWN>(c, a, cap, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,228 @@
+// C ABI of the fused MoE layer: host-side validation (before any HIP call),
+// workspace carving and the launch sequence route -> align -> GATE_UP GEMM
+// -> DOWN GEMM -> combine (FusedMoE vs MegaMoE post, section 3.1).
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "moe_launch.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopk = 16;
+constexpr int64_t kMaxPairs = 1 << 24;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_router(int32_t M, int32_t E, int32_t topk) {
+    if (M < 0 || E < 1 || topk < 1 || topk > E) return MOE_ERR_SHAPE;
+    if (E > kMaxExperts || topk > kMaxTopk) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)M * topk > kMaxPairs) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+bool valid_block_m(int32_t b) { return b == 1 || b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
+
+size_t elem_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : d == MOE_BF16 ? 2 : 1; }
+
+// bytes of the intermediate rows (act, y): f32 for the f32 path, bf16 otherwise
+size_t inter_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : 2; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int32_t fused_block_m(moe_dtype dtype, int32_t M, int32_t E, int32_t topk) {
+    if (dtype == MOE_F32) return 16;
+    const char* env = getenv("MOE_GEMM_PATH");
+    if (env && strcmp(env, "prefill") == 0) return 64;
+    if (env && strcmp(env, "decode") == 0) return 16;
+    const int64_t P = (int64_t)M * topk;
+    return (P / E > 64) ? 128 : 16;
+}
+
+struct Carve {
+    char* base;
+    size_t off;
+    template <typename T>
+    T* take(size_t n) {
+        T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+        off = round_up(off + n * sizeof(T), 256);
+        return p;
+    }
+};
+
+struct FusedLayout {
+    int32_t block_m;
+    int64_t cap;
+    size_t bytes;
+    int32_t* ids;
+    float* wts;
+    moe_align_bufs al;
+    void* act;
+    void* y;
+    float* amax;
+};
+
+FusedLayout fused_layout(char* ws, moe_dtype dtype, int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I) {
+    FusedLayout L;
+    const int64_t P = (int64_t)M * topk;
+    L.block_m = fused_block_m(dtype, M, E, topk);
+    L.cap = moe_align_capacity(M, topk, E, L.block_m);
+    Carve c{ws, 0};
+    L.ids = c.take<int32_t>(P);
+    L.wts = c.take<float>(P);
+    L.al.sorted_ids = c.take<int32_t>(L.cap);
+    L.al.tile_expert = c.take<int32_t>(L.cap / L.block_m);
+    L.al.expert_counts = c.take<int32_t>(E);
+    L.al.expert_offsets = c.take<int32_t>(E + 1);
+    L.al.active_experts = c.take<int32_t>(P < E ? P : E);
+    L.al.num_active = c.take<int32_t>(1);
+    L.amax = c.take<float>(1);
+    L.act = c.take<char>((size_t)P * I * inter_bytes(dtype));
+    L.y = c.take<char>((size_t)P * H * inter_bytes(dtype));
+    L.bytes = c.off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "invalid shape";
+        case MOE_ERR_UNSUPPORTED: return "unsupported size, dtype or block_m";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+        case MOE_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+moe_status moe_route(const float* logits, int32_t M, int32_t E, int32_t topk, int32_t renormalize,
+                     int32_t* topk_ids, float* topk_weights, void* stream) {
+    moe_status st = check_router(M, E, topk);
+    if (st != MOE_OK) return st;
+    if (M == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+    if (misaligned(logits) || misaligned(topk_ids) || misaligned(topk_weights)) return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_route(logits, M, E, topk, renormalize, topk_ids, topk_weights,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int64_t moe_align_capacity(int32_t M, int32_t topk, int32_t E, int32_t block_m) {
+    if (M < 0 || topk < 1 || E < 1 || block_m < 1) return -1;
+    const int64_t P = (int64_t)M * topk;
+    const int64_t act = P < E ? P : E;
+    const int64_t rows = P + act * (block_m - 1);
+    return (rows + block_m - 1) / block_m * block_m;
+}
+
+moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t E, int32_t block_m,
+                     moe_align_bufs out, void* stream) {
+    moe_status st = check_router(M, E, topk);
+    if (st != MOE_OK) return st;
+    if (!valid_block_m(block_m)) return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!topk_ids || !out.sorted_ids || !out.tile_expert || !out.expert_counts || !out.expert_offsets ||
+        !out.active_experts || !out.num_active)
+        return MOE_ERR_NULL;
+    if (misaligned(topk_ids) || misaligned(out.sorted_ids) || misaligned(out.tile_expert) ||
+        misaligned(out.expert_counts) || misaligned(out.expert_offsets) || misaligned(out.active_experts) ||
+        misaligned(out.num_active))
+        return MOE_ERR_ALIGNMENT;
+    const int64_t cap = moe_align_capacity(M, topk, E, block_m);
+    return hip_status(launch_align(topk_ids, M, topk, E, block_m, cap, out, nullptr,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, const float* a_scale,
+                            const void* w, const float* w_scale, const moe_align_bufs* al, int32_t M,
+                            int32_t topk, int32_t E, int32_t N, int32_t K, int32_t block_m, void* c,
+                            float* c_amax, void* stream) {
+    if (kind != MOE_GEMM_GATE_UP_SILU && kind != MOE_GEMM_DOWN) return MOE_ERR_UNSUPPORTED;
+    if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    moe_status st = check_router(M, E, topk);
+    if (st != MOE_OK) return st;
+    if (N < 1 || K < 1 || N % 128 || K % 128) return MOE_ERR_SHAPE;
+    if (kind == MOE_GEMM_GATE_UP_SILU && N % 256) return MOE_ERR_SHAPE;
+    if (!valid_block_m(block_m)) return MOE_ERR_UNSUPPORTED;
+    const bool fp8 = dtype == MOE_FP8_E4M3;
+    if (!fp8 && (a_scale || w_scale || c_amax)) return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!a || !w || !al || !c || !al->sorted_ids || !al->tile_expert || !al->expert_counts ||
+        !al->expert_offsets || !al->active_experts || !al->num_active)
+        return MOE_ERR_NULL;
+    if (fp8 && (!a_scale || !w_scale || (kind == MOE_GEMM_GATE_UP_SILU && !c_amax))) return MOE_ERR_NULL;
+    if (misaligned(a) || misaligned(w) || misaligned(c)) return MOE_ERR_ALIGNMENT;
+    GemmCall g{kind, dtype, a, a_scale, w, w_scale, *al, M, topk, E, N, K, block_m, c, c_amax};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fp8 && kind == MOE_GEMM_GATE_UP_SILU) {
+        hipError_t e = launch_fill_zero_f32(c_amax, 1, s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return hip_status(launch_grouped_gemm(g, s));
+}
+
+moe_status moe_combine(moe_dtype y_dtype, const void* y, const float* topk_weights, int32_t M,
+                       int32_t topk, int32_t H, moe_dtype out_dtype, void* out, void* stream) {
+    if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
+        return MOE_ERR_UNSUPPORTED;
+    if (M < 0 || topk < 1 || H < 1 || H % 8) return MOE_ERR_SHAPE;
+    if (topk > kMaxTopk) return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!y || !topk_weights || !out) return MOE_ERR_NULL;
+    if (misaligned(y) || misaligned(out)) return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_combine(y_dtype, y, topk_weights, M, topk, H, out_dtype, out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t fused_moe_workspace_size(moe_dtype dtype, int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I) {
+    if (M <= 0 || check_router(M, E, topk) != MOE_OK || H < 1 || I < 1) return 0;
+    return fused_layout(nullptr, dtype, M, E, topk, H, I).bytes;
+}
+
+moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
+                     const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
+                     int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize,
+                     void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    moe_status st = check_router(M, E, topk);
+    if (st != MOE_OK) return st;
+    if (H < 1 || I < 1 || H % 128 || I % 128) return MOE_ERR_SHAPE;
+    const bool fp8 = dtype == MOE_FP8_E4M3;
+    if (!fp8 && (x_scale || w1_scale || w2_scale)) return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!x || !router_logits || !w1 || !w2 || !out || !workspace) return MOE_ERR_NULL;
+    if (fp8 && (!x_scale || !w1_scale || !w2_scale)) return MOE_ERR_NULL;
+    if (misaligned(x) || misaligned(router_logits) || misaligned(w1) || misaligned(w2) || misaligned(out) ||
+        misaligned(topk_ids_out) || misaligned(topk_weights_out))
+        return MOE_ERR_ALIGNMENT;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_ERR_ALIGNMENT;
+    FusedLayout L = fused_layout(static_cast<char*>(workspace), dtype, M, E, topk, H, I);
+    if (workspace_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;
+    float* wts = topk_weights_out ? topk_weights_out : L.wts;
+    if (launch_route(router_logits, M, E, topk, renormalize, ids, wts, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_align(ids, M, topk, E, L.block_m, L.cap, L.al, fp8 ? L.amax : nullptr, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    const moe_dtype inter = dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
+    GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, x, x_scale, w1, w1_scale, L.al, M, topk, E, 2 * I, H,
+                L.block_m, L.act, fp8 ? L.amax : nullptr};
+    if (launch_grouped_gemm(g1, s) != hipSuccess) return MOE_ERR_HIP;
+    GemmCall g2{MOE_GEMM_DOWN, dtype, L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E, H, I,
+                L.block_m, L.y, nullptr};
+    if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal launchers behind the C ABI.  Arguments are validated by the
+// caller (moe_abi.hip) before any of these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Which grouped-GEMM kernel family serves a call.
+enum class GemmPath { kAuto = 0, kDecode = 1, kPrefill = 2 };
+
+hipError_t launch_route(const float* logits, int M, int E, int topk, int renormalize, int32_t* ids,
+                        float* weights, hipStream_t s);
+
+hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m, int64_t cap,
+                        const moe_align_bufs& out, float* zero_f32, hipStream_t s);
+
+hipError_t launch_fill_zero_f32(float* p, int n, hipStream_t s);
+
+struct GemmCall {
+    moe_gemm_kind kind;
+    moe_dtype dtype;
+    const void* a;
+    const float* a_scale;
+    const void* w;
+    const float* w_scale;
+    moe_align_bufs al;
+    int M, topk, E, N, K, block_m;
+    void* c;
+    float* c_amax;
+};
+
+// Kernel family chosen for a call (decode for few rows per expert, or when
+// block_m has no prefill tile; MOE_GEMM_PATH=decode|prefill overrides).
+GemmPath choose_gemm_path(const GemmCall& g);
+int prefill_supported_block_m(int block_m);
+
+hipError_t launch_grouped_gemm(const GemmCall& g, hipStream_t s);
+
+hipError_t launch_combine(moe_dtype y_dtype, const void* y, const float* w, int M, int topk, int H,
+                          moe_dtype out_dtype, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,259 @@
+// Top-k routing and token-to-expert alignment (FusedMoE vs MegaMoE post,
+// section 2 and section 3.1 steps 1-2).
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ route
+//
+// One wavefront per token.  Lane l holds logits l, l+64, l+128, l+192.
+// topk rounds of a wave-wide argmax on (value desc, index asc); the winner
+// is marked taken.  Comparison is IEEE, so +0 and -0 tie and the lower
+// index wins.  Weights are exp(l - l_max) over the chosen (or all) logits.
+
+struct Cand {
+    float v;
+    int i;
+};
+
+__device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+__global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits, int M, int E,
+                                                    int topk, int renormalize,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ weights) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= M) return;
+    const float* row = logits + (size_t)t * E;
+    float v[4];
+    bool live[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        int e = lane + 64 * q;
+        live[q] = e < E;
+        v[q] = live[q] ? row[e] : 0.0f;
+    }
+    float lmax = 0.0f, den = 0.0f;
+    float sel_v = 0.0f;  // this lane's record of slot j (lane j keeps slot j)
+    int sel_i = 0;
+    for (int j = 0; j < topk; ++j) {
+        float bv = 0.0f;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int e = lane + 64 * q;
+            if (live[q] && (bi == 0x7fffffff || beats(v[q], e, bv, bi))) {
+                bv = v[q];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            float ov = __shfl_xor(bv, off, 64);
+            int oi = __shfl_xor(bi, off, 64);
+            if (oi != 0x7fffffff && (bi == 0x7fffffff || beats(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        // bi is now wave-uniform
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane + 64 * q == bi) live[q] = false;
+        if (j == 0) lmax = bv;
+        if (lane == j) {
+            sel_v = bv;
+            sel_i = bi;
+        }
+    }
+    float ex = (lane < topk) ? __expf(sel_v - lmax) : 0.0f;
+    if (renormalize) {
+        den = ex;
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int e = lane + 64 * q;
+            if (e < E) den += __expf(row[e] - lmax);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+    if (lane < topk) {
+        ids[(size_t)t * topk + lane] = sel_i;
+        weights[(size_t)t * topk + lane] = ex / den;
+    }
+}
+
+hipError_t launch_route(const float* logits, int M, int E, int topk, int renormalize, int32_t* ids,
+                        float* weights, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    dim3 grid((M + 3) / 4);
+    hipLaunchKernelGGL(route_kernel, grid, dim3(256), 0, s, logits, M, E, topk, renormalize, ids,
+                       weights);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ align
+//
+// One workgroup of 1024 threads.  Counting sort with a stable scatter:
+//  1. LDS histogram of expert ids.
+//  2. Padded exclusive scan over experts (one wavefront, shuffles).
+//  3. Every position of sorted_ids past the real rows of its run gets the
+//     sentinel; tile_expert by binary search over the offsets.
+//  4. Pairs are scattered in chunks of 1024 in p order.  Inside a
+//     wavefront, lanes with the same expert are found with eight ballots
+//     (one per bit of the id) and ranked by popcount below the lane; the
+//     per-wavefront counts are prefix-summed across the 16 wavefronts
+//     through LDS, and a per-expert cursor carries over between chunks.
+//  Every write position is a function of topk_ids alone.
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / 64;
+constexpr int kMaxE = 256;
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    const int lane = __lane_id();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+__global__ void __launch_bounds__(kAlignThreads) align_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int block_m, int cap, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ active, int32_t* __restrict__ num_active,
+    float* __restrict__ zero_f32) {
+    __shared__ int cnt[kMaxE];
+    __shared__ int off[kMaxE + 1];
+    __shared__ int cursor[kMaxE];
+    __shared__ int wcnt[kAlignWaves][kMaxE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    if (tid == 0 && zero_f32) *zero_f32 = 0.0f;
+    for (int e = tid; e < kMaxE; e += kAlignThreads) cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kAlignThreads) {
+        int e = ids[p];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+
+    if (wave == 0) {
+        // lane handles experts 4*lane .. 4*lane+3
+        int c[4], pc[4], act[4];
+        int s = 0, a = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int e = 4 * lane + q;
+            c[q] = (e < E) ? cnt[e] : 0;
+            pc[q] = (c[q] + block_m - 1) / block_m * block_m;
+            act[q] = c[q] > 0;
+            s += pc[q];
+            a += act[q];
+        }
+        int incl = wave_incl_scan(s);
+        int aincl = wave_incl_scan(a);
+        int run = incl - s, arun = aincl - a;
+        int nact_total = __shfl(aincl, 63, 64);
+        int amax = P < E ? P : E;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int e = 4 * lane + q;
+            if (e < E) {
+                off[e] = run;
+                cursor[e] = run;
+                offsets_out[e] = run;
+                counts_out[e] = c[q];
+                if (act[q]) active[arun] = e;
+            }
+            run += pc[q];
+            arun += act[q];
+        }
+        if (lane == 63) {
+            off[E] = run;  // E <= 256 so 4*64 covers every expert
+            offsets_out[E] = run;
+            *num_active = nact_total;
+        }
+        for (int i = nact_total + lane; i < amax; i += 64) active[i] = -1;
+    }
+    __syncthreads();
+
+    const int total = off[E];
+    // sentinels and tile map: every row r that is not a real row of a run
+    for (int r = tid; r < cap; r += kAlignThreads) {
+        int e = -1;
+        if (r < total) {
+            int lo = 0, hi = E - 1;  // last e with off[e] <= r
+            while (lo < hi) {
+                int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= r) lo = mid; else hi = mid - 1;
+            }
+            e = lo;
+            if (r - off[e] >= cnt[e]) sorted[r] = P;
+        } else {
+            sorted[r] = P;
+        }
+        if (r % block_m == 0) tile_expert[r / block_m] = e;
+    }
+
+    // stable scatter, 1024 pairs per chunk
+    for (int base = 0; base < P; base += kAlignThreads) {
+        for (int i = tid; i < kAlignWaves * kMaxE; i += kAlignThreads) (&wcnt[0][0])[i] = 0;
+        __syncthreads();
+        const int p = base + tid;
+        int e = (p < P) ? ids[p] : -1;
+        const bool valid = (unsigned)e < (unsigned)E;
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            uint64_t bb = __ballot(valid && ((e >> b) & 1));
+            same &= ((e >> b) & 1) ? bb : ~bb;
+        }
+        const int rank = __popcll(same & lanemask_lt());
+        if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
+        __syncthreads();
+        if (valid) {
+            int pos = cursor[e] + rank;
+            for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+            sorted[pos] = p;
+        }
+        __syncthreads();
+        for (int x = tid; x < E; x += kAlignThreads) {
+            int sum = 0;
+            for (int w = 0; w < kAlignWaves; ++w) sum += wcnt[w][x];
+            cursor[x] += sum;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m, int64_t cap,
+                        const moe_align_bufs& out, float* zero_f32, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, M * topk, E, block_m,
+                       (int)cap, out.sorted_ids, out.tile_expert, out.expert_counts,
+                       out.expert_offsets, out.active_experts, out.num_active, zero_f32);
+    return hipGetLastError();
+}
+
+__global__ void fill_zero_f32_kernel(float* p, int n) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+hipError_t launch_fill_zero_f32(float* p, int n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -28,7 +28,8 @@ from dataclasses import dataclass, field
 import torch
 
 _M32 = 0xFFFFFFFF
-_CHUNK = 1 << 26  # elements per generation chunk (bounds temporaries)
+_CHUNK_GPU = 1 << 26  # elements per generation chunk on a GPU (bounds temporaries)
+_CHUNK_CPU = 1 << 18  # on the host: small enough that the int64 temporaries stay in cache
 
 # stream tags: one independent stream per tensor role
 S_X, S_LOGITS, S_WG, S_W1, S_W2, S_ACT, S_Y, S_WTS, S_IDS = range(1, 10)
@@ -81,8 +82,9 @@ def counter_normal(seed: int, stream: int, n: int, device, offset: int = 0) -> t
     out = torch.empty(n, dtype=torch.float64, device=device)
     two_pi = 2.0 * math.pi
     inv32 = 1.0 / 4294967296.0
-    for s in range(0, n, _CHUNK):
-        e = min(n, s + _CHUNK)
+    chunk = _CHUNK_CPU if torch.device(device).type == "cpu" else _CHUNK_GPU
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
         idx = torch.arange(offset + s, offset + e, dtype=torch.int64, device=device)
         u1 = (_words(idx, seed, stream, 0) + 1).to(torch.float64) * inv32  # (0, 1]
         u2 = _words(idx, seed, stream, 1).to(torch.float64) * inv32  # [0, 1)
