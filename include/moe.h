@@ -120,7 +120,8 @@ moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t E
  *  al, block_m: the output of moe_align for the same topk_ids and block_m.
  *  Rows of a expert's run are read through al->sorted_ids; only the first
  *  expert_counts[e] rows of each run are written to c.
- * Errors as for the other calls; K and N must be multiples of 128. */
+ * Errors as for the other calls; K and N must be multiples of 128 (K of 256
+ * for MOE_FP8_E4M3). */
 moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, const float* a_scale,
                             const void* w, const float* w_scale, const moe_align_bufs* al, int32_t M,
                             int32_t topk, int32_t E, int32_t N, int32_t K, int32_t block_m, void* c,
@@ -147,6 +148,7 @@ size_t fused_moe_workspace_size(moe_dtype dtype, int32_t M, int32_t E, int32_t t
  *  out            device [M][H]: float32 for MOE_F32, bfloat16 otherwise
  *  topk_ids_out, topk_weights_out  optional device [M][topk] copies of the
  *                 routing result (NULL to skip)
+ *  H and I must be multiples of 128 (of 256 for MOE_FP8_E4M3).
  *  workspace      device, >= fused_moe_workspace_size(...) bytes, 256-byte
  *                 aligned; its contents on entry do not matter. */
 moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,

@@ -94,16 +94,51 @@ __device__ __forceinline__ void amax_publish(float m, float* dst) {
 }
 
 // ----------------------------------------------------------------- decode
+//
+// Work split: blockIdx.y is an active-expert slot, blockIdx.x a block of
+// weight rows of that expert (G groups of four 16-row tiles; for GATE_UP a
+// group is 16+16 gate rows and the matching 16+16 up rows).  A step is 256
+// bytes of every row of one group; the four wavefronts take steps
+// round-robin along K and reduce their partial sums through LDS at the end.
+// Each lane issues 16-byte loads at byte 64u + 16g of the step span (g = lane
+// group, u = 0..3), so one load instruction reads 64 contiguous bytes of each
+// of 16 rows; the K order this induces is applied to the token operand too.
+// The next step's loads are issued before the current step's MFMAs
+// (register double buffer, pinned by scheduling barriers) so a wavefront
+// always has a full step of weights in flight.
 
 constexpr int kDecThreads = 256;
-constexpr int kDecU = 4;  // MFMAs per row tile per K step: each lane holds 32 consecutive elements
+constexpr int kDecSpan = 256;  // bytes of each row per step
 
 template <int KIND, int DT, int NT>
+struct DecodeTokens {
+    // one 16-byte MFMA operand chunk of the token rows for load u of a step
+    __device__ static __forceinline__ uint4 load(const char* brow, size_t step_off, int u, float qs) {
+        if constexpr (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) {
+            // act is bf16: 16 elements = 32 bytes, quantised on load
+            const uint4* p = reinterpret_cast<const uint4*>(brow + 2 * (step_off + u * 64));
+            uint2 lo = quant8(p[0], qs), hi = quant8(p[1], qs);
+            return uint4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+            return *reinterpret_cast<const uint4*>(brow + step_off + u * 64);
+        }
+    }
+};
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_chunk(const uint4& a, const uint4& b, f32x4 c) {
+    if constexpr (DT == MOE_BF16) {
+        return Opnd<MOE_BF16>::mfma(a, b, c);
+    } else {
+        c = Opnd<MOE_FP8_E4M3>::mfma(uint2{a.x, a.y}, uint2{b.x, b.y}, c);
+        return Opnd<MOE_FP8_E4M3>::mfma(uint2{a.z, a.w}, uint2{b.z, b.w}, c);
+    }
+}
+
+template <int KIND, int DT, int NT, int G>
 __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
-    using O = Opnd<DT>;
-    using chunk = typename O::chunk;
-    constexpr int kElem = O::kElemBytes;
-    constexpr int kStep = 128;  // K elements per step (4 lane groups x 32)
+    constexpr int kElem = Opnd<DT>::kElemBytes;
+    constexpr int T = 4;  // 16-row tiles per group
 
     const int slot = blockIdx.y;
     if (slot >= *g.num_active) return;
@@ -113,25 +148,28 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int lr = lane & 15;  // row within a 16-row tile / token column
-    const int lg = lane >> 4;  // lane group: 32-element span inside a step
+    const int lr = lane & 15;  // row within a tile / token column
+    const int lg = lane >> 4;  // lane group
     const int K = g.K, N = g.N;
     const int I = N / 2;
-    const int nsteps = K / kStep;
+    const size_t rowb = (size_t)K * kElem;
+    const int nks = (int)(rowb / kDecSpan);  // steps along K per group
+    const int total = G * nks;
 
-    // weight rows of the four 16-row tiles
-    const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 32 : blockIdx.x * 64;
-    const char* wbase = reinterpret_cast<const char*>(g.w) + (size_t)e * N * K * kElem;
-    const char* arow[4];
+    const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 32 * G : blockIdx.x * 64 * G;
+    const char* wbase = reinterpret_cast<const char*>(g.w) + (size_t)e * N * rowb + lg * 16;
+    // byte offset of this lane's row of tile t in group 0 (groups add gstride rows)
+    size_t arow[T];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int t = 0; t < T; ++t) {
         int row;
         if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
-            row = (i < 2) ? n0 + 16 * i + lr : I + n0 + 16 * (i - 2) + lr;
+            row = (t < 2) ? n0 + 16 * t + lr : I + n0 + 16 * (t - 2) + lr;
         else
-            row = n0 + 16 * i + lr;
-        arow[i] = wbase + ((size_t)row * K + lg * 32) * kElem;
+            row = n0 + 16 * t + lr;
+        arow[t] = (size_t)row * rowb;
     }
+    const size_t gstride = (size_t)((KIND == MOE_GEMM_GATE_UP_SILU) ? 32 : 64) * rowb;
 
     float scale = 1.0f, qs = 1.0f;
     if constexpr (DT == MOE_FP8_E4M3) {
@@ -142,93 +180,110 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
             scale = qs * g.w_scale[e];
         }
     }
+    // token-row byte stride and the lane's offset inside a step
+    const size_t brow_bytes = (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) ? (size_t)K * 2 : rowb;
+    const int blane = lg * 16;  // in operand bytes (fp8 act: in elements, scaled x2 inside the loader)
 
-    extern __shared__ f32x4 red[];  // [4 waves][4 tiles][NT][64 lanes]
+    extern __shared__ f32x4 red[];  // [4 waves][G*T tiles][NT][64 lanes]
     float amax = 0.0f;
 
     for (int pass = 0; pass < cnt; pass += NT * 16) {
         const int ntiles = min(NT, (cnt - pass + 15) / 16);
-        // source rows of this lane's token columns
         const char* brow[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-            int r = min(pass + c * 16 + lr, cnt - 1);
-            int p = g.sorted[base + r];
-            if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
-                brow[c] = reinterpret_cast<const char*>(g.a) + ((size_t)(p / g.topk) * K + lg * 32) * kElem;
-            else if constexpr (DT == MOE_FP8_E4M3)
-                brow[c] = reinterpret_cast<const char*>(g.a) + ((size_t)p * K + lg * 32) * 2;  // bf16 act
-            else
-                brow[c] = reinterpret_cast<const char*>(g.a) + ((size_t)p * K + lg * 32) * kElem;
+            const int r = min(pass + c * 16 + lr, cnt - 1);
+            const int p = g.sorted[base + r];
+            const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
+            brow[c] = reinterpret_cast<const char*>(g.a) + (size_t)src * brow_bytes +
+                      ((KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) ? 2 * blane : blane);
         }
 
-        f32x4 acc[4][NT];
+        f32x4 acc[G][T][NT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-            for (int c = 0; c < NT; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int c = 0; c < NT; ++c) acc[gi][t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        for (int s = wave; s < nsteps; s += 4) {
-            const size_t koff = (size_t)s * kStep;
-            chunk av[4][kDecU];
+        uint4 a0[T][4], b0[NT][4], a1[T][4], b1[NT][4];
+        auto load = [&](uint4 (&a)[T][4], uint4 (&b)[NT][4], int s) {
+            const int gi = s / nks, ks = s % nks;
+            const char* wg = wbase + gi * gstride + (size_t)ks * kDecSpan;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int t = 0; t < T; ++t)
 #pragma unroll
-                for (int u = 0; u < kDecU; ++u)
-                    av[i][u] = *reinterpret_cast<const chunk*>(arow[i] + (koff + u * 8) * kElem);
-            chunk bv[NT][kDecU];
+                for (int u = 0; u < 4; ++u) a[t][u] = *reinterpret_cast<const uint4*>(wg + arow[t] + u * 64);
+            const size_t soff = (size_t)ks * kDecSpan;
 #pragma unroll
-            for (int c = 0; c < NT; ++c) {
-                if (c < ntiles) {
+            for (int c = 0; c < NT; ++c)
+                if (c < ntiles)
 #pragma unroll
-                    for (int u = 0; u < kDecU; ++u) {
-                        if constexpr (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) {
-                            uint4 h = *reinterpret_cast<const uint4*>(brow[c] + (koff + u * 8) * 2);
-                            bv[c][u] = __builtin_bit_cast(chunk, quant8(h, qs));
-                        } else {
-                            bv[c][u] = *reinterpret_cast<const chunk*>(brow[c] + (koff + u * 8) * kElem);
-                        }
+                    for (int u = 0; u < 4; ++u) b[c][u] = DecodeTokens<KIND, DT, NT>::load(brow[c], soff, u, qs);
+        };
+
+        int s = wave;
+        if (s < total) load(a0, b0, s);
+        for (; s < total; s += 4) {
+            const bool nx = s + 4 < total;
+            if (nx) load(a1, b1, s + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            const int gi = s / nks;
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg) {
+                if (gg != gi) continue;
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    if (c < ntiles) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+#pragma unroll
+                            for (int t = 0; t < T; ++t) acc[gg][t][c] = mfma_chunk<DT>(a0[t][u], b0[c][u], acc[gg][t][c]);
                     }
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (nx) {
 #pragma unroll
-            for (int c = 0; c < NT; ++c) {
-                if (c < ntiles) {
+                for (int t = 0; t < T; ++t)
 #pragma unroll
-                    for (int u = 0; u < kDecU; ++u)
+                    for (int u = 0; u < 4; ++u) a0[t][u] = a1[t][u];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[i][c] = O::mfma(av[i][u], bv[c][u], acc[i][c]);
-                }
+                for (int c = 0; c < NT; ++c)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) b0[c][u] = b1[c][u];
             }
         }
 
         // K-split reduction across the four wavefronts
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-            for (int c = 0; c < NT; ++c) red[((wave * 4 + i) * NT + c) * 64 + lane] = acc[i][c];
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int c = 0; c < NT; ++c) red[((wave * G * T + gi * T + t) * NT + c) * 64 + lane] = acc[gi][t][c];
         __syncthreads();
 
-        const int units = (KIND == MOE_GEMM_GATE_UP_SILU) ? 2 * ntiles : 4 * ntiles;
+        constexpr int kPer = (KIND == MOE_GEMM_GATE_UP_SILU) ? 2 : 4;  // output tiles per group
+        const int units = G * kPer * ntiles;
         for (int u = wave; u < units; u += 4) {
-            const int r = pass + (u / ((KIND == MOE_GEMM_GATE_UP_SILU) ? 2 : 4)) * 16 + lr;
-            const int c = u / ((KIND == MOE_GEMM_GATE_UP_SILU) ? 2 : 4);
+            const int c = u / (G * kPer);
+            const int gq = u % (G * kPer);
+            const int gi = gq / kPer, q = gq % kPer;
+            const int r = pass + c * 16 + lr;
             if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
-                const int q = u % 2;
                 f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    gs += red[((w * 4 + q) * NT + c) * 64 + lane];
-                    us += red[((w * 4 + q + 2) * NT + c) * 64 + lane];
+                    gs += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
+                    us += red[((w * G * T + gi * T + q + 2) * NT + c) * 64 + lane];
                 }
                 if (r < cnt) {
                     const int p = g.sorted[base + r];
                     float o[4];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float gv = gs[v] * scale, uv = us[v] * scale;
-                        o[v] = silu(gv) * uv;
-                    }
+                    for (int v = 0; v < 4; ++v) o[v] = silu(gs[v] * scale) * (us[v] * scale);
                     uint2 pk;
                     pk.x = pack_bf2(o[0], o[1]);
                     pk.y = pack_bf2(o[2], o[3]);
@@ -238,17 +293,16 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
                         amax = fmaxf(amax, fabsf(bf2f(pk.y & 0xffff)));
                         amax = fmaxf(amax, fabsf(bf2f(pk.y >> 16)));
                     }
-                    const int n = n0 + 16 * q + 4 * lg;
+                    const int n = n0 + gi * 32 + 16 * q + 4 * lg;
                     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * I + n) = pk;
                 }
             } else {
-                const int i = u % 4;
                 f32x4 ys = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int w = 0; w < 4; ++w) ys += red[((w * 4 + i) * NT + c) * 64 + lane];
+                for (int w = 0; w < 4; ++w) ys += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
                 if (r < cnt) {
                     const int p = g.sorted[base + r];
-                    const int n = n0 + 16 * i + 4 * lg;
+                    const int n = n0 + gi * 64 + 16 * q + 4 * lg;
                     uint2 pk;
                     pk.x = pack_bf2(ys[0] * scale, ys[1] * scale);
                     pk.y = pack_bf2(ys[2] * scale, ys[3] * scale);
@@ -484,22 +538,38 @@ GemmPath choose_gemm_path(const GemmCall& g) {
     return (per_expert > 64 && pre_ok) ? GemmPath::kPrefill : GemmPath::kDecode;
 }
 
-template <int KIND, int DT, int NT>
-static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, hipStream_t s) {
-    const int nblk = (KIND == MOE_GEMM_GATE_UP_SILU) ? (a.N / 2) / 32 : a.N / 64;
-    const size_t lds = sizeof(f32x4) * 4 * 4 * NT * 64;
-    hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT>), dim3(nblk, nslots), dim3(kDecThreads), lds, s, a);
+template <int KIND, int DT, int NT, int G>
+static hipError_t launch_decode_ntg(const GemmArgs& a, int nslots, hipStream_t s) {
+    const int rows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 * G : 64 * G;  // output columns per workgroup
+    const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
+    const size_t lds = sizeof(f32x4) * 4 * G * 4 * NT * 64;
+    hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT, G>), dim3(ncols / rows, nslots), dim3(kDecThreads), lds, s,
+                       a);
     return hipGetLastError();
+}
+
+template <int KIND, int DT, int NT>
+static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_est, hipStream_t s) {
+    // two row groups per workgroup when that still leaves >= 2 workgroups per CU
+    const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
+    const int rows2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? 64 : 128;
+    if (NT < 4 && ncols % rows2 == 0 && (long)(ncols / rows2) * active_est >= 512)
+        return launch_decode_ntg<KIND, DT, NT, 2>(a, nslots, s);
+    return launch_decode_ntg<KIND, DT, NT, 1>(a, nslots, s);
 }
 
 template <int KIND, int DT>
 static hipError_t launch_decode(const GemmArgs& a, int M, int topk, int E, hipStream_t s) {
     const long P = (long)M * topk;
     const int nslots = (int)(P < E ? P : E);
-    const long avg = (P + E - 1) / E;
-    if (avg <= 10) return launch_decode_nt<KIND, DT, 1>(a, nslots, s);
-    if (avg <= 24) return launch_decode_nt<KIND, DT, 2>(a, nslots, s);
-    return launch_decode_nt<KIND, DT, 4>(a, nslots, s);
+    // expected active experts and a high quantile of rows per expert under
+    // uniform routing pick the token tiles per pass
+    const double avg = (double)P / E;
+    const double hi = avg + 3.0 * __builtin_sqrt(avg) + 1.0;
+    const long active_est = nslots;
+    if (hi <= 16.0) return launch_decode_nt<KIND, DT, 1>(a, nslots, active_est, s);
+    if (hi <= 32.0) return launch_decode_nt<KIND, DT, 2>(a, nslots, active_est, s);
+    return launch_decode_nt<KIND, DT, 4>(a, nslots, active_est, s);
 }
 
 template <int KIND, int DT>

@@ -154,6 +154,7 @@ moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, 
     if (kind == MOE_GEMM_GATE_UP_SILU && N % 256) return MOE_ERR_SHAPE;
     if (!valid_block_m(block_m)) return MOE_ERR_UNSUPPORTED;
     const bool fp8 = dtype == MOE_FP8_E4M3;
+    if (fp8 && K % 256) return MOE_ERR_SHAPE;
     if (!fp8 && (a_scale || w_scale || c_amax)) return MOE_ERR_UNSUPPORTED;
     if (M == 0) return MOE_OK;
     if (!a || !w || !al || !c || !al->sorted_ids || !al->tile_expert || !al->expert_counts ||
@@ -198,6 +199,7 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
     if (st != MOE_OK) return st;
     if (H < 1 || I < 1 || H % 128 || I % 128) return MOE_ERR_SHAPE;
     const bool fp8 = dtype == MOE_FP8_E4M3;
+    if (fp8 && (H % 256 || I % 256)) return MOE_ERR_SHAPE;
     if (!fp8 && (x_scale || w1_scale || w2_scale)) return MOE_ERR_UNSUPPORTED;
     if (M == 0) return MOE_OK;
     if (!x || !router_logits || !w1 || !w2 || !out || !workspace) return MOE_ERR_NULL;

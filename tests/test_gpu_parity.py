@@ -124,7 +124,7 @@ def _gemm_case(dtype, E, k, H, I, M, seed=0):
 
 
 GEMM_CASES = [("bf16", 8, 2, 256, 256, 40), ("bf16", 16, 4, 512, 384, 100), ("bf16", 4, 2, 128, 128, 300),
-              ("fp8", 8, 2, 256, 256, 40), ("fp8", 16, 4, 512, 384, 100), ("f32", 8, 2, 256, 512, 16),
+              ("fp8", 8, 2, 256, 256, 40), ("fp8", 16, 4, 512, 512, 100), ("f32", 8, 2, 256, 512, 16),
               ("bf16", 128, 8, 256, 128, 16), ("bf16", 8, 2, 1024, 256, 1)]
 
 
