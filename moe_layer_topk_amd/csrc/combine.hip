@@ -65,3 +65,59 @@ hipError_t launch_combine(moe_dtype y_dtype, const void* y, const float* w, int 
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// Split-K variant: the down projection left ksplit float32 partial rows per
+// pair; y[p] = sum over z ascending, then out[t] = sum_j w[t,j] y[t*k+j] with
+// j ascending, so the result does not depend on scheduling.
+template <int ODT>
+__global__ void __launch_bounds__(256) combine_partials_kernel(const float* __restrict__ ypart, int ksplit,
+                                                               size_t zstride, const float* __restrict__ w,
+                                                               int topk, int H, void* __restrict__ out) {
+    const int t = blockIdx.x;
+    const int h = (blockIdx.y * 256 + threadIdx.x) * 8;
+    if (h >= H) return;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < topk; ++j) {
+        const float wj = w[(size_t)t * topk + j];
+        const float* row = ypart + ((size_t)t * topk + j) * H + h;
+        float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int z = 0; z < ksplit; ++z) {
+            const float4* p = reinterpret_cast<const float4*>(row + z * zstride);
+            const float4 a = p[0], b = p[1];
+            y[0] += a.x; y[1] += a.y; y[2] += a.z; y[3] += a.w;
+            y[4] += b.x; y[5] += b.y; y[6] += b.z; y[7] += b.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, y[i], acc[i]);
+    }
+    if (ODT == MOE_BF16) {
+        uint4 o;
+        o.x = pack_bf2(acc[0], acc[1]);
+        o.y = pack_bf2(acc[2], acc[3]);
+        o.z = pack_bf2(acc[4], acc[5]);
+        o.w = pack_bf2(acc[6], acc[7]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * H + h) = o;
+    } else {
+        float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (size_t)t * H + h);
+        p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+}
+
+hipError_t launch_combine_partials(const float* ypart, int ksplit, const float* w, int M, int topk, int H,
+                                   moe_dtype out_dtype, void* out, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    dim3 grid(M, (H / 8 + 255) / 256);
+    const size_t zstride = (size_t)M * topk * H;
+    if (out_dtype == MOE_BF16)
+        hipLaunchKernelGGL((combine_partials_kernel<MOE_BF16>), grid, dim3(256), 0, s, ypart, ksplit, zstride, w,
+                           topk, H, out);
+    else
+        hipLaunchKernelGGL((combine_partials_kernel<MOE_F32>), grid, dim3(256), 0, s, ypart, ksplit, zstride, w,
+                           topk, H, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

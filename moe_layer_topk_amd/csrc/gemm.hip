@@ -85,6 +85,8 @@ struct GemmArgs {
     int topk, N, K, P;
     void* c;
     float* c_amax;
+    int ksplit;    // decode DOWN only: K ranges handled by blockIdx.z
+    float* cpart;  // non-null: DOWN writes float32 partials [ksplit][P][N] here instead of c
 };
 
 __device__ __forceinline__ void amax_publish(float m, float* dst) {
@@ -153,7 +155,10 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
     const int K = g.K, N = g.N;
     const int I = N / 2;
     const size_t rowb = (size_t)K * kElem;
-    const int nks = (int)(rowb / kDecSpan);  // steps along K per group
+    const int nks_all = (int)(rowb / kDecSpan);  // steps along K per group
+    // split-K: this workgroup covers steps [ks0, ks0 + nks) of every group
+    const int ks0 = (int)((long)blockIdx.z * nks_all / g.ksplit);
+    const int nks = (int)((long)(blockIdx.z + 1) * nks_all / g.ksplit) - ks0;
     const int total = G * nks;
 
     const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 32 * G : blockIdx.x * 64 * G;
@@ -209,7 +214,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
 
         uint4 a0[T][4], b0[NT][4], a1[T][4], b1[NT][4];
         auto load = [&](uint4 (&a)[T][4], uint4 (&b)[NT][4], int s) {
-            const int gi = s / nks, ks = s % nks;
+            const int gi = s / nks, ks = ks0 + s % nks;
             const char* wg = wbase + gi * gstride + (size_t)ks * kDecSpan;
 #pragma unroll
             for (int t = 0; t < T; ++t)
@@ -300,7 +305,11 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
                 f32x4 ys = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int w = 0; w < 4; ++w) ys += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
-                if (r < cnt) {
+                if (r < cnt && g.cpart) {
+                    const int p = g.sorted[base + r];
+                    const int n = n0 + gi * 64 + 16 * q + 4 * lg;
+                    *reinterpret_cast<f32x4*>(g.cpart + ((size_t)blockIdx.z * g.P + p) * N + n) = ys * scale;
+                } else if (r < cnt) {
                     const int p = g.sorted[base + r];
                     const int n = n0 + gi * 64 + 16 * q + 4 * lg;
                     uint2 pk;
@@ -489,6 +498,187 @@ __global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
     if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) amax_publish(amax, g.c_amax);
 }
 
+// ------------------------------------------------------- prefill (bf16)
+//
+// Many rows per expert.  Block tile 128 sorted rows x 256 weight rows x 64 K,
+// four wavefronts each computing 64 x 128 with v_mfma_f32_32x32x16_bf16
+// (tokens on the row operand, weights on the column operand: Eq. 1).
+// Operands reach LDS with direct-to-LDS 16-byte loads (no register
+// staging) into a three-stage ring, so two K stages are always in flight
+// while the third is multiplied; one barrier per stage.  Each 128-byte LDS
+// row holds its eight 16-byte chunks in XOR-swizzled order (chunk c of row
+// r at c ^ (r & 7)) so the fragment reads of 32 rows spread over the
+// banks; the swizzle is applied by the choice of each lane's source chunk.
+// Tile order: a flat (n-tile, m-tile) index with m fastest, cut into eight
+// contiguous ranges, one per XCD (workgroups are dealt to XCDs round
+// robin), so the row tiles that share a weight tile run on one XCD and the
+// weight tile is fetched from HBM once into that XCD's L2.
+
+constexpr int kP2BM = 128, kP2BN = 256, kP2BK = 64, kP2Stages = 3;
+constexpr int kP2RowBytes = kP2BK * 2;                        // 128
+constexpr int kP2ABytes = kP2BM * kP2RowBytes;                // 16 KB
+constexpr int kP2BBytes = kP2BN * kP2RowBytes;                // 32 KB
+constexpr int kP2StageBytes = kP2ABytes + kP2BBytes;          // 48 KB
+constexpr int kP2Xcds = 8;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+
+// wait until at most n vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+template <int KIND>
+__global__ void __launch_bounds__(256) gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
+    extern __shared__ __attribute__((aligned(1024))) char p2_lds[];
+    const int nb = m_tiles * n_tiles;
+    const int per = (nb + kP2Xcds - 1) / kP2Xcds;
+    const int t = (blockIdx.x % kP2Xcds) * per + blockIdx.x / kP2Xcds;
+    if (t >= nb) return;
+    const int ntile = t / m_tiles, mtile = t % m_tiles;
+    const int e = g.tile_expert[mtile];
+    if (e < 0) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to M0
+    const int wm = wave >> 1, wn = wave & 1;
+    const int K = g.K, N = g.N, I = N / 2, P = g.P;
+    const size_t rowb = (size_t)K * 2;
+
+    // ---- per-lane sources of this wave's load instructions (8 rows each)
+    // A rows [32*wave, 32*wave + 32): 4 instructions; B rows [64*wave, +64): 8.
+    const int lrow = lane >> 3;                 // row within the 8-row group
+    const int lchunk = (lane & 7) ^ lrow;       // logical chunk landing in this lane's slot
+    const char* asrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 32 * wave + 8 * j + lrow;
+        int p = g.sorted[mtile * kP2BM + r];
+        if (p >= P) p = g.sorted[mtile * kP2BM];  // padding row: any valid row (its output is dropped)
+        const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
+        asrc[j] = reinterpret_cast<const char*>(g.a) + (size_t)src * rowb + lchunk * 16;
+    }
+    const char* wbase = reinterpret_cast<const char*>(g.w) + (size_t)e * N * rowb;
+    const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? ntile * 128 : ntile * 256;
+    const char* bsrc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = 64 * wave + 8 * j + lrow;  // B row in the tile
+        int row;
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
+            row = (r < 128) ? n0 + r : I + n0 + (r - 128);
+        else
+            row = n0 + r;
+        bsrc[j] = wbase + (size_t)row * rowb + lchunk * 16;
+    }
+
+    auto issue = [&](int kt) {
+        char* st = p2_lds + (kt % kP2Stages) * kP2StageBytes;
+        const size_t koff = (size_t)kt * kP2RowBytes;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lds_dma16(asrc[j] + koff, st + (32 * wave + 8 * j) * kP2RowBytes);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) lds_dma16(bsrc[j] + koff, st + kP2ABytes + (64 * wave + 8 * j) * kP2RowBytes);
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // fragment rows (LDS row index) of this wave
+    int arow[2], brow[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) arow[i] = wm * 64 + 32 * i + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
+            brow[j] = (j < 2) ? wn * 64 + 32 * j + (lane & 31) : 128 + wn * 64 + 32 * (j - 2) + (lane & 31);
+        else
+            brow[j] = wn * 128 + 32 * j + (lane & 31);
+    }
+    const int khalf = lane >> 5;  // which 8-element half of a 16-wide K slice
+
+    const int nk = K / kP2BK;
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk) wait_vm<12>(); else wait_vm<0>();
+        __syncthreads();
+        if (kt + 2 < nk) issue(kt + 2);
+        const char* st = p2_lds + (kt % kP2Stages) * kP2StageBytes;
+        const char* sa = st;
+        const char* sb = st + kP2ABytes;
+#pragma unroll
+        for (int ks = 0; ks < kP2BK / 16; ++ks) {
+            const int c = ks * 2 + khalf;  // logical 16-byte chunk
+            bf16x8_t af[2], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t*>(sa + arow[i] * kP2RowBytes + ((c ^ (arow[i] & 7)) << 4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + brow[j] * kP2RowBytes + ((c ^ (brow[j] & 7)) << 4));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // ---- epilogue: lane holds C[8*(v/4) + 4*(lane/32) + v%4][lane%32] of each 32x32 tile
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int p = g.sorted[mtile * kP2BM + r];
+            if (p >= P) continue;
+            if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
+                    const int n = n0 + wn * 64 + 32 * j + (lane & 31);
+                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * I + n] = f2bf(silu(gv) * uv);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = n0 + wn * 128 + 32 * j + (lane & 31);
+                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * N + n] = f2bf(acc[i][j][v]);
+                }
+            }
+        }
+    }
+}
+
+template <int KIND>
+static hipError_t launch_prefill2(const GemmArgs& a, int64_t cap, hipStream_t s) {
+    const int m_tiles = (int)(cap / kP2BM);
+    const int n_tiles = (KIND == MOE_GEMM_GATE_UP_SILU) ? (a.N / 2) / 128 : a.N / 256;
+    const int nb = m_tiles * n_tiles;
+    const int grid = (nb + kP2Xcds - 1) / kP2Xcds * kP2Xcds;
+    const size_t lds = (size_t)kP2Stages * kP2StageBytes;
+    // LDS above the default dynamic limit must be requested once per kernel
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill2_kernel<KIND>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gemm_prefill2_kernel<KIND>), dim3(grid), dim3(256), lds, s, a, m_tiles, n_tiles);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- f32
 //
 // Plain fp32 path: one thread per (sorted row, output column), dot products
@@ -528,6 +718,22 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g, int block_m, 
 
 int prefill_supported_block_m(int block_m) { return block_m == 64 || block_m == 128; }
 
+int down_ksplit(moe_dtype dtype, int M, int topk, int E, int N, int K, int block_m) {
+    if (dtype == MOE_F32 || M == 0) return 1;
+    GemmCall probe{MOE_GEMM_DOWN, dtype, nullptr, nullptr, nullptr, nullptr, {}, M, topk, E, N, K, block_m,
+                   nullptr, nullptr};
+    if (choose_gemm_path(probe) != GemmPath::kDecode) return 1;
+    const long P = (long)M * topk;
+    const long slots = P < E ? P : E;
+    const long wgs = (long)(N / 64) * slots;  // one row group per workgroup
+    if (wgs >= 512) return 1;
+    const int steps = (int)((long)K * (dtype == MOE_BF16 ? 2 : 1) / kDecSpan);
+    int ks = (int)((768 + wgs - 1) / wgs);
+    if (ks > 8) ks = 8;
+    if (ks > steps) ks = steps;
+    return ks < 1 ? 1 : ks;
+}
+
 GemmPath choose_gemm_path(const GemmCall& g) {
     const char* env = getenv("MOE_GEMM_PATH");
     const bool pre_ok = prefill_supported_block_m(g.block_m);
@@ -543,8 +749,8 @@ static hipError_t launch_decode_ntg(const GemmArgs& a, int nslots, hipStream_t s
     const int rows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 * G : 64 * G;  // output columns per workgroup
     const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
     const size_t lds = sizeof(f32x4) * 4 * G * 4 * NT * 64;
-    hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT, G>), dim3(ncols / rows, nslots), dim3(kDecThreads), lds, s,
-                       a);
+    hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT, G>), dim3(ncols / rows, nslots, a.ksplit), dim3(kDecThreads),
+                       lds, s, a);
     return hipGetLastError();
 }
 
@@ -553,7 +759,7 @@ static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_es
     // two row groups per workgroup when that still leaves >= 2 workgroups per CU
     const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
     const int rows2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? 64 : 128;
-    if (NT < 4 && ncols % rows2 == 0 && (long)(ncols / rows2) * active_est >= 512)
+    if (NT < 4 && a.ksplit == 1 && ncols % rows2 == 0 && (long)(ncols / rows2) * active_est >= 512)
         return launch_decode_ntg<KIND, DT, NT, 2>(a, nslots, s);
     return launch_decode_ntg<KIND, DT, NT, 1>(a, nslots, s);
 }
@@ -593,6 +799,8 @@ static hipError_t launch_kind(const GemmCall& c, const GemmArgs& a, int64_t cap,
     }
     const GemmPath path = choose_gemm_path(c);
     if (c.dtype == MOE_BF16) {
+        const int n2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? (c.N / 2) % 128 : c.N % 256;
+        if (path == GemmPath::kPrefill && c.block_m == kP2BM && n2 == 0) return launch_prefill2<KIND>(a, cap, s);
         if (path == GemmPath::kPrefill) return launch_prefill<KIND, MOE_BF16>(a, c.block_m, cap, s);
         return launch_decode<KIND, MOE_BF16>(a, c.M, c.topk, c.E, s);
     }
@@ -619,6 +827,8 @@ hipError_t launch_grouped_gemm(const GemmCall& c, hipStream_t s) {
     a.P = c.M * c.topk;
     a.c = c.c;
     a.c_amax = c.c_amax;
+    a.ksplit = c.ksplit;
+    a.cpart = c.cpart;
     const int64_t cap = moe_align_capacity(c.M, c.topk, c.E, c.block_m);
     if (c.kind == MOE_GEMM_GATE_UP_SILU) return launch_kind<MOE_GEMM_GATE_UP_SILU>(c, a, cap, s);
     return launch_kind<MOE_GEMM_DOWN>(c, a, cap, s);

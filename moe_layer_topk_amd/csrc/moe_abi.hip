@@ -57,6 +57,7 @@ struct Carve {
 
 struct FusedLayout {
     int32_t block_m;
+    int32_t ksplit;  // K split of the DOWN GEMM (partials summed by the combine)
     int64_t cap;
     size_t bytes;
     int32_t* ids;
@@ -64,6 +65,7 @@ struct FusedLayout {
     moe_align_bufs al;
     void* act;
     void* y;
+    float* ypart;
     float* amax;
 };
 
@@ -84,6 +86,8 @@ FusedLayout fused_layout(char* ws, moe_dtype dtype, int32_t M, int32_t E, int32_
     L.amax = c.take<float>(1);
     L.act = c.take<char>((size_t)P * I * inter_bytes(dtype));
     L.y = c.take<char>((size_t)P * H * inter_bytes(dtype));
+    L.ksplit = down_ksplit(dtype, M, topk, E, H, I, L.block_m);
+    L.ypart = L.ksplit > 1 ? c.take<float>((size_t)L.ksplit * P * H) : nullptr;
     L.bytes = c.off;
     return L;
 }
@@ -222,8 +226,9 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
                 L.block_m, L.act, fp8 ? L.amax : nullptr};
     if (launch_grouped_gemm(g1, s) != hipSuccess) return MOE_ERR_HIP;
     GemmCall g2{MOE_GEMM_DOWN, dtype, L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E, H, I,
-                L.block_m, L.y, nullptr};
+                L.block_m, L.y, nullptr, L.ksplit, L.ypart};
     if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
+    if (L.ksplit > 1) return hip_status(launch_combine_partials(L.ypart, L.ksplit, wts, M, topk, H, inter, out, s));
     return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));
 }
 

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -31,6 +31,8 @@ struct GemmCall {
     int M, topk, E, N, K, block_m;
     void* c;
     float* c_amax;
+    int ksplit = 1;         // decode DOWN: split of K across workgroups
+    float* cpart = nullptr;  // with ksplit > 1: float32 partials [ksplit][P][N] instead of c
 };
 
 // Kernel family chosen for a call (decode for few rows per expert, or when
@@ -39,6 +41,13 @@ GemmPath choose_gemm_path(const GemmCall& g);
 int prefill_supported_block_m(int block_m);
 
 hipError_t launch_grouped_gemm(const GemmCall& g, hipStream_t s);
+
+// K split the fused layer uses for the DOWN GEMM (1 when the decode kernel
+// already has enough workgroups, or when the prefill kernel serves the call).
+int down_ksplit(moe_dtype dtype, int M, int topk, int E, int N, int K, int block_m);
+
+hipError_t launch_combine_partials(const float* ypart, int ksplit, const float* w, int M, int topk, int H,
+                                   moe_dtype out_dtype, void* out, hipStream_t s);
 
 hipError_t launch_combine(moe_dtype y_dtype, const void* y, const float* w, int M, int topk, int H,
                           moe_dtype out_dtype, void* out, hipStream_t s);

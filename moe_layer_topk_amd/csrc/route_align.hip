@@ -12,23 +12,15 @@ namespace moe {
 // is marked taken.  Comparison is IEEE, so +0 and -0 tie and the lower
 // index wins.  Weights are exp(l - l_max) over the chosen (or all) logits.
 
-struct Cand {
-    float v;
-    int i;
-};
-
 __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
-__global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits, int M, int E,
-                                                    int topk, int renormalize,
-                                                    int32_t* __restrict__ ids,
-                                                    float* __restrict__ weights) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= M) return;
-    const float* row = logits + (size_t)t * E;
+// Routes token `t` with the calling wavefront; lane j < topk ends up holding
+// slot j (returned through *sel_out / *w_out for lanes < topk).
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int topk, int renormalize,
+                                            int* sel_out, float* w_out) {
+    const int lane = __lane_id();
     float v[4];
     bool live[4];
 #pragma unroll
@@ -38,7 +30,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
         v[q] = live[q] ? row[e] : 0.0f;
     }
     float lmax = 0.0f, den = 0.0f;
-    float sel_v = 0.0f;  // this lane's record of slot j (lane j keeps slot j)
+    float sel_v = 0.0f;
     int sel_i = 0;
     for (int j = 0; j < topk; ++j) {
         float bv = 0.0f;
@@ -82,9 +74,23 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+    *sel_out = sel_i;
+    *w_out = ex / den;
+}
+
+__global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits, int M, int E,
+                                                    int topk, int renormalize,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ weights) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= M) return;
+    int sel;
+    float w;
+    route_token(logits + (size_t)t * E, E, topk, renormalize, &sel, &w);
     if (lane < topk) {
-        ids[(size_t)t * topk + lane] = sel_i;
-        weights[(size_t)t * topk + lane] = ex / den;
+        ids[(size_t)t * topk + lane] = sel;
+        weights[(size_t)t * topk + lane] = w;
     }
 }
 
@@ -92,8 +98,7 @@ hipError_t launch_route(const float* logits, int M, int E, int topk, int renorma
                         float* weights, hipStream_t s) {
     if (M == 0) return hipSuccess;
     dim3 grid((M + 3) / 4);
-    hipLaunchKernelGGL(route_kernel, grid, dim3(256), 0, s, logits, M, E, topk, renormalize, ids,
-                       weights);
+    hipLaunchKernelGGL(route_kernel, grid, dim3(256), 0, s, logits, M, E, topk, renormalize, ids, weights);
     return hipGetLastError();
 }
 
@@ -125,11 +130,11 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
-__global__ void __launch_bounds__(kAlignThreads) align_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int block_m, int cap, int32_t* __restrict__ sorted,
-    int32_t* __restrict__ tile_expert, int32_t* __restrict__ counts_out,
-    int32_t* __restrict__ offsets_out, int32_t* __restrict__ active, int32_t* __restrict__ num_active,
-    float* __restrict__ zero_f32) {
+template <typename GetId>
+__device__ __forceinline__ void align_core(GetId get_id, int P, int E, int block_m, int cap,
+                                           int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
+                                           int32_t* __restrict__ counts_out, int32_t* __restrict__ offsets_out,
+                                           int32_t* __restrict__ active, int32_t* __restrict__ num_active) {
     __shared__ int cnt[kMaxE];
     __shared__ int off[kMaxE + 1];
     __shared__ int cursor[kMaxE];
@@ -138,11 +143,10 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    if (tid == 0 && zero_f32) *zero_f32 = 0.0f;
     for (int e = tid; e < kMaxE; e += kAlignThreads) cnt[e] = 0;
     __syncthreads();
     for (int p = tid; p < P; p += kAlignThreads) {
-        int e = ids[p];
+        int e = get_id(p);
         if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
@@ -210,7 +214,7 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(
         for (int i = tid; i < kAlignWaves * kMaxE; i += kAlignThreads) (&wcnt[0][0])[i] = 0;
         __syncthreads();
         const int p = base + tid;
-        int e = (p < P) ? ids[p] : -1;
+        int e = (p < P) ? get_id(p) : -1;
         const bool valid = (unsigned)e < (unsigned)E;
         uint64_t same = __ballot(valid);
 #pragma unroll
@@ -234,6 +238,16 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(
         }
         __syncthreads();
     }
+}
+
+__global__ void __launch_bounds__(kAlignThreads) align_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int block_m, int cap, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ active, int32_t* __restrict__ num_active,
+    float* __restrict__ zero_f32) {
+    if (threadIdx.x == 0 && zero_f32) *zero_f32 = 0.0f;
+    align_core([&](int p) { return ids[p]; }, P, E, block_m, cap, sorted, tile_expert, counts_out, offsets_out,
+               active, num_active);
 }
 
 hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m, int64_t cap,

@@ -129,15 +129,15 @@ GEMM_CASES = [("bf16", 8, 2, 256, 256, 40), ("bf16", 16, 4, 512, 384, 100), ("bf
 
 
 @pytest.mark.parametrize("dtype,E,k,H,I,M", GEMM_CASES)
-@pytest.mark.parametrize("path", ["decode", "prefill"])
+@pytest.mark.parametrize("path", ["decode", "prefill", "prefill128"])
 def test_grouped_gemm(dev, monkeypatch, dtype, E, k, H, I, M, path):
     import moe_layer_topk_amd as moe
     say(f"gemm {dtype} E={E} k={k} H={H} I={I} M={M} path={path}")
-    monkeypatch.setenv("MOE_GEMM_PATH", path)
+    monkeypatch.setenv("MOE_GEMM_PATH", path.replace("128", ""))
     cfg, w, b = _gemm_case(dtype, E, k, H, I, M)
     rid, _ = oracle.route(b["logits"], k)
     ids = torch.from_numpy(rid).to(dev)
-    bm = 64 if path == "prefill" else 16
+    bm = {"prefill": 64, "prefill128": 128}.get(path, 16)
     al = moe.moe_align(ids, E, bm)
     P = M * k
     pairs = np.arange(P)
@@ -253,6 +253,19 @@ def test_paths_agree_eq2_identity(dev, monkeypatch):
     torch.cuda.synchronize()
     d = (outs["decode"] - outs["prefill"]).abs().max().item()
     assert d <= 1e-2 * outs["decode"].abs().max().item()
+
+
+@pytest.mark.parametrize("E,k,H,I,M", [(16, 8, 512, 256, 200), (8, 2, 1024, 512, 700), (4, 1, 256, 128, 1000)])
+def test_fused_prefill_shapes(dev, E, k, H, I, M):
+    """Shapes with more than 64 rows per expert take the LDS-ring prefill kernel."""
+    cfg = replace(CONFIGS["finegrained_bf16"], E=E, topk=k, H=H, I=I, router="zipf")
+    say(f"fused prefill E={E} k={k} H={H} I={I} M={M}")
+    check_layer(cfg, M, dev, tokens=np.arange(0, M, 7))
+
+
+def test_fused_layer_full_prefill(dev):
+    say("fused mixtral_prefill_bf16 M=4096 (sampled tokens)")
+    check_layer(CONFIGS["mixtral_prefill_bf16"], 4096, dev, tokens=[0, 1, 2, 1000, 2047, 3000, 4094, 4095])
 
 
 def test_fused_deterministic(dev):
