@@ -35,9 +35,37 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_decode_bf16")
     ap.add_argument("--M", type=int, default=None, help="tokens per batch (default: the largest decode batch)")
-    ap.add_argument("--sweep", default="1,8,32", help="extra batch sizes timed for context")
+    ap.add_argument("--sweep", default="", help="extra batch sizes timed for context, e.g. 1,8,32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only run a plain device-to-device copy of MB MiB three times (counter calibration)")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: measured counter traffic is only reported for the build it was taken on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "moe_layer_topk_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, M: int):
+    """HBM bytes per gate/up launch from profiles/traffic.json (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    scaled by the same counters on a copy of known size), if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    entry = t.get("gate_up", {}).get(f"{workload}/M={M}")
+    return None if entry is None else entry.get("bytes_per_launch")
 
 
 def layer_bytes(cfg, M, n_active, wbytes, xbytes, obytes):
@@ -63,6 +91,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
 
     import moe_layer_topk_amd as moe
     from workloads import CONFIGS, layer_batch, layer_weights
@@ -190,7 +228,8 @@ def main():
         "config": {"workload": cfg.name, "M": M, "E": cfg.E, "topk": cfg.topk, "hidden": cfg.H,
                    "intermediate": cfg.I, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "gate_up grouped GEMM", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(cfg.name, M)},
         "cpu_baseline": cpu,
         "layer": {k2: main_res[k2] for k2 in ("roofline_frac", "layer_hbm_frac", "layer_mfma_frac", "kernel_us",
                                               "staged_ms_per_step", "gate_up_GBs", "down_GBs", "active_experts")},

@@ -500,26 +500,23 @@ __global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
 
 // ------------------------------------------------------- prefill (bf16)
 //
-// Many rows per expert.  Block tile 128 sorted rows x 256 weight rows x 64 K,
-// four wavefronts each computing 64 x 128 with v_mfma_f32_32x32x16_bf16
-// (tokens on the row operand, weights on the column operand: Eq. 1).
-// Operands reach LDS with direct-to-LDS 16-byte loads (no register
-// staging) into a three-stage ring, so two K stages are always in flight
-// while the third is multiplied; one barrier per stage.  Each 128-byte LDS
-// row holds its eight 16-byte chunks in XOR-swizzled order (chunk c of row
-// r at c ^ (r & 7)) so the fragment reads of 32 rows spread over the
-// banks; the swizzle is applied by the choice of each lane's source chunk.
-// Tile order: a flat (n-tile, m-tile) index with m fastest, cut into eight
-// contiguous ranges, one per XCD (workgroups are dealt to XCDs round
-// robin), so the row tiles that share a weight tile run on one XCD and the
-// weight tile is fetched from HBM once into that XCD's L2.
+// Many rows per expert.  Block tile BM sorted rows x BN weight rows x BK, four
+// wavefronts in a 2x2 grid, each computing (BM/2) x (BN/2) with
+// v_mfma_f32_32x32x16_bf16 (tokens on the row operand, weights on the
+// column operand: Eq. 1).  Operands reach LDS with direct-to-LDS 16-byte
+// loads (no register staging) into an ST-stage ring, so ST-1 K stages are in
+// flight while one is multiplied; one barrier per stage.  The 16-byte chunks
+// of each LDS row are XOR-swizzled so that the fragment reads of 16
+// consecutive rows at one logical chunk fall into distinct bank groups of
+// the 64 x 4-byte banks; the swizzle is applied by the choice of each lane's
+// source chunk.  Tile order: a flat index over (weight-tile group, row tile,
+// weight tile in group), cut into eight contiguous ranges, one per XCD
+// (workgroups are dealt to XCDs round robin), so the row tiles sharing a
+// weight tile run on one XCD, the weight tile is fetched from HBM once into
+// that XCD's L2, and each token tile is reused by the group's weight tiles.
 
-constexpr int kP2BM = 128, kP2BN = 256, kP2BK = 64, kP2Stages = 3;
-constexpr int kP2RowBytes = kP2BK * 2;                        // 128
-constexpr int kP2ABytes = kP2BM * kP2RowBytes;                // 16 KB
-constexpr int kP2BBytes = kP2BN * kP2RowBytes;                // 32 KB
-constexpr int kP2StageBytes = kP2ABytes + kP2BBytes;          // 48 KB
 constexpr int kP2Xcds = 8;
+constexpr int kP2GroupN = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -534,129 +531,189 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+template <int L>
+__device__ __forceinline__ void wait_vm_runtime(int stages_outstanding) {
+    switch (stages_outstanding) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<L>(); break;
+        case 2: wait_vm<2 * L < 64 ? 2 * L : 63>(); break;
+        default: wait_vm<3 * L < 64 ? 3 * L : 63>(); break;
+    }
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-template <int KIND>
-__global__ void __launch_bounds__(256) gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
+template <int BM_, int BN_, int BK_, int ST_, int WM_ = 2, int WN_ = 2>
+struct P2Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, ST = ST_;
+    static constexpr int WM = WM_, WN = WN_, Waves = WM * WN, Threads = 64 * Waves;
+    static constexpr int RowBytes = BK * 2;
+    static constexpr int Chunks = BK / 8;                // 16-byte chunks per LDS row
+    static constexpr int RowsPerLoad = 64 / Chunks;      // rows one 1 KB load instruction fills
+    static constexpr int ABytes = BM * RowBytes, BBytes = BN * RowBytes;
+    static constexpr int StageBytes = ABytes + BBytes;
+    static constexpr int IdsOffset = ST * StageBytes;
+    static constexpr int LdsBytes = IdsOffset + BM * 4;
+    static constexpr int ALoads = BM / RowsPerLoad / Waves;  // per wave per stage
+    static constexpr int BLoads = BN / RowsPerLoad / Waves;
+    static constexpr int L = ALoads + BLoads;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
+    static constexpr int TM = WTM / 32, TN = WTN / 32;       // 32x32 MFMA tiles per wave
+    // physical chunk of logical chunk c in row r: rows in groups of 16/Chunks
+    // share a bank window of 256 bytes
+    __device__ static __forceinline__ int swz(int c, int r) { return c ^ ((r / (16 / Chunks)) % Chunks); }
+    static_assert(ALoads * RowsPerLoad * Waves == BM && BLoads * RowsPerLoad * Waves == BN, "load split");
+    static_assert(TN % 2 == 0, "gate/up pairing needs an even number of column tiles");
+    static_assert(LdsBytes <= 160 * 1024, "LDS");
+};
+
+// One wavefront per SIMD (the LDS ring fills the CU): registers are not
+// rationed for occupancy.
+template <int KIND, class C>
+__global__ void __launch_bounds__(C::Threads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
     extern __shared__ __attribute__((aligned(1024))) char p2_lds[];
     const int nb = m_tiles * n_tiles;
     const int per = (nb + kP2Xcds - 1) / kP2Xcds;
     const int t = (blockIdx.x % kP2Xcds) * per + blockIdx.x / kP2Xcds;
     if (t >= nb) return;
-    const int ntile = t / m_tiles, mtile = t % m_tiles;
+    // flat order: groups of kP2GroupN weight tiles; inside a group the row
+    // tiles advance slowest, so the blocks an XCD runs together cover a few
+    // row tiles x a few weight tiles and both operands are reused from L2
+    const int ng = t / (kP2GroupN * m_tiles);
+    const int gw = min(kP2GroupN, n_tiles - ng * kP2GroupN);
+    const int rem = t - ng * kP2GroupN * m_tiles;
+    const int mtile = rem / gw, ntile = ng * kP2GroupN + rem % gw;
     const int e = g.tile_expert[mtile];
     if (e < 0) return;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to M0
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WN, wn = wave % C::WN;
     const int K = g.K, N = g.N, I = N / 2, P = g.P;
     const size_t rowb = (size_t)K * 2;
+    int* ids_s = reinterpret_cast<int*>(p2_lds + C::IdsOffset);
+    for (int i = tid; i < C::BM; i += C::Threads) ids_s[i] = g.sorted[mtile * C::BM + i];
 
-    // ---- per-lane sources of this wave's load instructions (8 rows each)
-    // A rows [32*wave, 32*wave + 32): 4 instructions; B rows [64*wave, +64): 8.
-    const int lrow = lane >> 3;                 // row within the 8-row group
-    const int lchunk = (lane & 7) ^ lrow;       // logical chunk landing in this lane's slot
-    const char* asrc[4];
+    // ---- per-lane sources of this wave's load instructions.  Lane l fills
+    // physical chunk l % Chunks of row l / Chunks of the instruction's rows,
+    // so it loads the logical chunk the swizzle (an involution in c) maps there.
+    const int lrow = lane / C::Chunks, lphys = lane % C::Chunks;
+    const char* asrc[C::ALoads];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 32 * wave + 8 * j + lrow;
-        int p = g.sorted[mtile * kP2BM + r];
-        if (p >= P) p = g.sorted[mtile * kP2BM];  // padding row: any valid row (its output is dropped)
+    for (int j = 0; j < C::ALoads; ++j) {
+        const int r = (wave * C::ALoads + j) * C::RowsPerLoad + lrow;
+        int p = g.sorted[mtile * C::BM + r];
+        if (p >= P) p = g.sorted[mtile * C::BM];  // padding row: any valid row (its output is dropped)
         const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
-        asrc[j] = reinterpret_cast<const char*>(g.a) + (size_t)src * rowb + lchunk * 16;
+        asrc[j] = reinterpret_cast<const char*>(g.a) + (size_t)src * rowb + C::swz(lphys, r) * 16;
     }
     const char* wbase = reinterpret_cast<const char*>(g.w) + (size_t)e * N * rowb;
-    const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? ntile * 128 : ntile * 256;
-    const char* bsrc[8];
+    const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? ntile * (C::BN / 2) : ntile * C::BN;
+    const char* bsrc[C::BLoads];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = 64 * wave + 8 * j + lrow;  // B row in the tile
+    for (int j = 0; j < C::BLoads; ++j) {
+        const int r = (wave * C::BLoads + j) * C::RowsPerLoad + lrow;  // B row in the tile
         int row;
         if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
-            row = (r < 128) ? n0 + r : I + n0 + (r - 128);
+            row = (r < C::BN / 2) ? n0 + r : I + n0 + (r - C::BN / 2);
         else
             row = n0 + r;
-        bsrc[j] = wbase + (size_t)row * rowb + lchunk * 16;
+        bsrc[j] = wbase + (size_t)row * rowb + C::swz(lphys, r) * 16;
     }
 
     auto issue = [&](int kt) {
-        char* st = p2_lds + (kt % kP2Stages) * kP2StageBytes;
-        const size_t koff = (size_t)kt * kP2RowBytes;
+        char* st = p2_lds + (kt % C::ST) * C::StageBytes;
+        const size_t koff = (size_t)kt * C::RowBytes;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lds_dma16(asrc[j] + koff, st + (32 * wave + 8 * j) * kP2RowBytes);
+        for (int j = 0; j < C::ALoads; ++j)
+            lds_dma16(asrc[j] + koff, st + (wave * C::ALoads + j) * C::RowsPerLoad * C::RowBytes);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) lds_dma16(bsrc[j] + koff, st + kP2ABytes + (64 * wave + 8 * j) * kP2RowBytes);
+        for (int j = 0; j < C::BLoads; ++j)
+            lds_dma16(bsrc[j] + koff, st + C::ABytes + (wave * C::BLoads + j) * C::RowsPerLoad * C::RowBytes);
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[C::TM][C::TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     // fragment rows (LDS row index) of this wave
-    int arow[2], brow[4];
+    int arow[C::TM], brow[C::TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) arow[i] = wm * 64 + 32 * i + (lane & 31);
+    for (int i = 0; i < C::TM; ++i) arow[i] = wm * C::WTM + 32 * i + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < C::TN; ++j) {
+        // GATE_UP: a wave's columns are WTN/2 gate rows and the matching up rows
         if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
-            brow[j] = (j < 2) ? wn * 64 + 32 * j + (lane & 31) : 128 + wn * 64 + 32 * (j - 2) + (lane & 31);
+            brow[j] = (j < C::TN / 2) ? wn * (C::WTN / 2) + 32 * j + (lane & 31)
+                                      : C::BN / 2 + wn * (C::WTN / 2) + 32 * (j - C::TN / 2) + (lane & 31);
         else
-            brow[j] = wn * 128 + 32 * j + (lane & 31);
+            brow[j] = wn * C::WTN + 32 * j + (lane & 31);
     }
     const int khalf = lane >> 5;  // which 8-element half of a 16-wide K slice
 
-    const int nk = K / kP2BK;
-    issue(0);
-    if (nk > 1) issue(1);
+    const int nk = K / C::BK;
+#pragma unroll
+    for (int s0 = 0; s0 < C::ST - 1; ++s0)
+        if (s0 < nk) issue(s0);
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) wait_vm<12>(); else wait_vm<0>();
+        const int ahead = min(C::ST - 2, nk - 1 - kt);  // later stages already issued
+        wait_vm_runtime<C::L>(ahead);
         __syncthreads();
-        if (kt + 2 < nk) issue(kt + 2);
-        const char* st = p2_lds + (kt % kP2Stages) * kP2StageBytes;
+        if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1);
+        const char* st = p2_lds + (kt % C::ST) * C::StageBytes;
         const char* sa = st;
-        const char* sb = st + kP2ABytes;
-#pragma unroll
-        for (int ks = 0; ks < kP2BK / 16; ++ks) {
+        const char* sb = st + C::ABytes;
+        // fragments double buffered across the 16-wide K substeps: the reads
+        // for substep ks+1 are interleaved with the MFMAs of substep ks
+        bf16x8_t af[2][C::TM], bfr[2][C::TN];
+        auto read_frags = [&](int buf, int ks) {
             const int c = ks * 2 + khalf;  // logical 16-byte chunk
-            bf16x8_t af[2], bfr[4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t*>(sa + arow[i] * kP2RowBytes + ((c ^ (arow[i] & 7)) << 4));
+            for (int i = 0; i < C::TM; ++i)
+                af[buf][i] = *reinterpret_cast<const bf16x8_t*>(sa + arow[i] * C::RowBytes + (C::swz(c, arow[i]) << 4));
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + brow[j] * kP2RowBytes + ((c ^ (brow[j] & 7)) << 4));
+            for (int j = 0; j < C::TN; ++j)
+                bfr[buf][j] = *reinterpret_cast<const bf16x8_t*>(sb + brow[j] * C::RowBytes + (C::swz(c, brow[j]) << 4));
+        };
+        read_frags(0, 0);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int ks = 0; ks < C::BK / 16; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < C::BK / 16) read_frags(cur ^ 1, ks + 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     // ---- epilogue: lane holds C[8*(v/4) + 4*(lane/32) + v%4][lane%32] of each 32x32 tile
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int r = wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            const int p = g.sorted[mtile * kP2BM + r];
+            const int r = wm * C::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int p = ids_s[r];
             if (p >= P) continue;
             if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
-                    const int n = n0 + wn * 64 + 32 * j + (lane & 31);
+                for (int j = 0; j < C::TN / 2; ++j) {
+                    const float gv = acc[i][j][v], uv = acc[i][j + C::TN / 2][v];
+                    const int n = n0 + wn * (C::WTN / 2) + 32 * j + (lane & 31);
                     reinterpret_cast<uint16_t*>(g.c)[(size_t)p * I + n] = f2bf(silu(gv) * uv);
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = n0 + wn * 128 + 32 * j + (lane & 31);
+                for (int j = 0; j < C::TN; ++j) {
+                    const int n = n0 + wn * C::WTN + 32 * j + (lane & 31);
                     reinterpret_cast<uint16_t*>(g.c)[(size_t)p * N + n] = f2bf(acc[i][j][v]);
                 }
             }
@@ -664,18 +721,24 @@ __global__ void __launch_bounds__(256) gemm_prefill2_kernel(GemmArgs g, int m_ti
     }
 }
 
+// block shape of the LDS-ring prefill kernel
+using PrefillCfg = P2Cfg<128, 256, 64, 3>;
+constexpr int kP2BM = PrefillCfg::BM;
+
 template <int KIND>
 static hipError_t launch_prefill2(const GemmArgs& a, int64_t cap, hipStream_t s) {
-    const int m_tiles = (int)(cap / kP2BM);
-    const int n_tiles = (KIND == MOE_GEMM_GATE_UP_SILU) ? (a.N / 2) / 128 : a.N / 256;
+    using C = PrefillCfg;
+    const int m_tiles = (int)(cap / C::BM);
+    const int n_tiles = (KIND == MOE_GEMM_GATE_UP_SILU) ? (a.N / 2) / (C::BN / 2) : a.N / C::BN;
     const int nb = m_tiles * n_tiles;
     const int grid = (nb + kP2Xcds - 1) / kP2Xcds * kP2Xcds;
-    const size_t lds = (size_t)kP2Stages * kP2StageBytes;
     // LDS above the default dynamic limit must be requested once per kernel
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill2_kernel<KIND>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_prefill2_kernel<KIND, C>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        C::LdsBytes);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemm_prefill2_kernel<KIND>), dim3(grid), dim3(256), lds, s, a, m_tiles, n_tiles);
+    hipLaunchKernelGGL((gemm_prefill2_kernel<KIND, C>), dim3(grid), dim3(C::Threads), C::LdsBytes, s, a, m_tiles,
+                       n_tiles);
     return hipGetLastError();
 }
 
@@ -799,7 +862,7 @@ static hipError_t launch_kind(const GemmCall& c, const GemmArgs& a, int64_t cap,
     }
     const GemmPath path = choose_gemm_path(c);
     if (c.dtype == MOE_BF16) {
-        const int n2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? (c.N / 2) % 128 : c.N % 256;
+        const int n2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? (c.N / 2) % (PrefillCfg::BN / 2) : c.N % PrefillCfg::BN;
         if (path == GemmPath::kPrefill && c.block_m == kP2BM && n2 == 0) return launch_prefill2<KIND>(a, cap, s);
         if (path == GemmPath::kPrefill) return launch_prefill<KIND, MOE_BF16>(a, c.block_m, cap, s);
         return launch_decode<KIND, MOE_BF16>(a, c.M, c.topk, c.E, s);

@@ -58,6 +58,7 @@ def lib():
             "oracle_align_capacity": (i64, [i64, i32, i32, i32]),
             "oracle_align": (i32, [P, i64, i32, i32, i32, i64, P, P, P, P, P, P]),
             "oracle_act_amax": (i32, [i32, P, P, P, P, P, i64, i32, i32, i64, i64, i32, P]),
+            "oracle_act_amax_per_token": (i32, [i32, P, P, P, P, P, i64, i32, i32, i64, i64, i32, P]),
             "oracle_moe": (i32, [i32, P, P, P, P, P, P, P, i64, i32, i32, i64, i64, i32, dbl, P, i64, P]),
             "oracle_pairs_gate_up": (i32, [i32, P, P, P, i64, i32, P, P, i32, i64, i64, P, i64, P]),
             "oracle_pairs_down": (i32, [i32, i32, P, dbl, P, i64, P, P, i32, i64, i64, P, i64, P]),
@@ -165,6 +166,18 @@ def act_amax(dtype, x, x_scale, logits, w1, w1_scale, topk, renormalize=True) ->
                                  _ptr(_f32(w1_scale)), M, E, topk, H, twoI // 2, int(renormalize),
                                  _ptr(out)), "act_amax")
     return float(out[0])
+
+
+def act_amax_per_token(dtype, x, x_scale, logits, w1, w1_scale, topk, renormalize=True):
+    """float64 [M]: largest |intermediate| over each token's pairs."""
+    xn, lg, w1n = _np(x), np.ascontiguousarray(_np(logits), np.float32), _np(w1)
+    M, H = xn.shape
+    E, twoI, _ = w1n.shape
+    out = np.zeros(M, np.float64)
+    _check(lib().oracle_act_amax_per_token(_DT[dtype], _ptr(xn), _ptr(_f32(x_scale)), _ptr(lg), _ptr(w1n),
+                                           _ptr(_f32(w1_scale)), M, E, topk, H, twoI // 2, int(renormalize),
+                                           _ptr(out)), "act_amax_per_token")
+    return out
 
 
 def moe_layer(dtype, x, x_scale, logits, w1, w1_scale, w2, w2_scale, topk, renormalize=True,

@@ -280,6 +280,44 @@ int oracle_act_amax(int dtype, const void* x, const float* x_scale, const float*
     return err;
 }
 
+/* Per-token version of oracle_act_amax: amax_out[t] = largest |a| over the
+ * token's k pairs, so the batch statistic of any prefix of tokens is the max
+ * of a prefix of this array. */
+int oracle_act_amax_per_token(int dtype, const void* x, const float* x_scale, const float* logits,
+                              const void* w1, const float* w1_scale, int64_t M, int E, int k, int64_t H,
+                              int64_t I, int renorm, double* amax_out) {
+    if (M < 0 || E < 1 || k < 1 || k > E || H < 1 || I < 1) return OR_EARG;
+    size_t eb = elem_bytes(dtype);
+    int err = 0;
+#pragma omp parallel
+    {
+        double* a = (double*)malloc(sizeof(double) * I);
+        int32_t ids[256];
+        double w[256];
+        if (!a) err = OR_ENOMEM;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < M; ++t) {
+            if (!a) continue;
+            double local = 0.0;
+            int rc = route_one(logits + t * E, E, k, renorm, ids, w);
+            if (rc) {
+                err = rc;
+                continue;
+            }
+            for (int j = 0; j < k; ++j) {
+                int e = ids[j];
+                oracle_gate_up(dtype, (const char*)x + (size_t)t * H * eb, sc(x_scale, 0),
+                               (const char*)w1 + (size_t)e * 2 * I * H * eb, sc(w1_scale, e), H, I, a);
+                for (int64_t n = 0; n < I; ++n)
+                    if (fabs(a[n]) > local) local = fabs(a[n]);
+            }
+            amax_out[t] = local;
+        }
+        free(a);
+    }
+    return err;
+}
+
 /* The whole layer for the tokens listed in `tokens` (n_tok entries):
  * out[i][h] for token tokens[i].  For fp8, act_amax is the batch-wide
  * statistic from oracle_act_amax. */
