@@ -87,6 +87,7 @@ struct GemmArgs {
     float* c_amax;
     int ksplit;    // decode DOWN only: K ranges handled by blockIdx.z
     float* cpart;  // non-null: DOWN writes float32 partials [ksplit][P][N] here instead of c
+    int act_q8;    // fp8 DOWN: a holds e4m3 codes already quantised with amax/448
 };
 
 __device__ __forceinline__ void amax_publish(float m, float* dst) {
@@ -112,11 +113,13 @@ __device__ __forceinline__ void amax_publish(float m, float* dst) {
 constexpr int kDecThreads = 256;
 constexpr int kDecSpan = 256;  // bytes of each row per step
 
-template <int KIND, int DT, int NT>
+// AQ: the DOWN operand is already e4m3 (quantised once by quant_act_kernel)
+template <int KIND, int DT, bool AQ>
 struct DecodeTokens {
+    static constexpr bool kBf16Act = KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3 && !AQ;
     // one 16-byte MFMA operand chunk of the token rows for load u of a step
     __device__ static __forceinline__ uint4 load(const char* brow, size_t step_off, int u, float qs) {
-        if constexpr (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) {
+        if constexpr (kBf16Act) {
             // act is bf16: 16 elements = 32 bytes, quantised on load
             const uint4* p = reinterpret_cast<const uint4*>(brow + 2 * (step_off + u * 64));
             uint2 lo = quant8(p[0], qs), hi = quant8(p[1], qs);
@@ -137,8 +140,9 @@ __device__ __forceinline__ f32x4 mfma_chunk(const uint4& a, const uint4& b, f32x
     }
 }
 
-template <int KIND, int DT, int NT, int G>
+template <int KIND, int DT, int NT, int G, bool AQ>
 __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
+    using Tok = DecodeTokens<KIND, DT, AQ>;
     constexpr int kElem = Opnd<DT>::kElemBytes;
     constexpr int T = 4;  // 16-row tiles per group
 
@@ -186,7 +190,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
         }
     }
     // token-row byte stride and the lane's offset inside a step
-    const size_t brow_bytes = (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) ? (size_t)K * 2 : rowb;
+    const size_t brow_bytes = Tok::kBf16Act ? (size_t)K * 2 : rowb;
     const int blane = lg * 16;  // in operand bytes (fp8 act: in elements, scaled x2 inside the loader)
 
     extern __shared__ f32x4 red[];  // [4 waves][G*T tiles][NT][64 lanes]
@@ -201,7 +205,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
             const int p = g.sorted[base + r];
             const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
             brow[c] = reinterpret_cast<const char*>(g.a) + (size_t)src * brow_bytes +
-                      ((KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) ? 2 * blane : blane);
+                      (Tok::kBf16Act ? 2 * blane : blane);
         }
 
         f32x4 acc[G][T][NT];
@@ -225,7 +229,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
             for (int c = 0; c < NT; ++c)
                 if (c < ntiles)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) b[c][u] = DecodeTokens<KIND, DT, NT>::load(brow[c], soff, u, qs);
+                    for (int u = 0; u < 4; ++u) b[c][u] = Tok::load(brow[c], soff, u, qs);
         };
 
         int s = wave;
@@ -373,7 +377,7 @@ __global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
     const char* asrc[kAChunks];
     const char* bsrc[kBChunks];
     int adst[kAChunks], bdst[kBChunks];
-    const bool a_is_bf16_act = (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3);
+    const bool a_is_bf16_act = (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) && !g.act_q8;
 #pragma unroll
     for (int q = 0; q < kAChunks; ++q) {
         int id = tid + q * kPreThreads;
@@ -807,14 +811,22 @@ GemmPath choose_gemm_path(const GemmCall& g) {
     return (per_expert > 64 && pre_ok) ? GemmPath::kPrefill : GemmPath::kDecode;
 }
 
-template <int KIND, int DT, int NT, int G>
-static hipError_t launch_decode_ntg(const GemmArgs& a, int nslots, hipStream_t s) {
+template <int KIND, int DT, int NT, int G, bool AQ>
+static hipError_t launch_decode_ntga(const GemmArgs& a, int nslots, hipStream_t s) {
     const int rows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 * G : 64 * G;  // output columns per workgroup
     const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
     const size_t lds = sizeof(f32x4) * 4 * G * 4 * NT * 64;
-    hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT, G>), dim3(ncols / rows, nslots, a.ksplit), dim3(kDecThreads),
-                       lds, s, a);
+    hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT, G, AQ>), dim3(ncols / rows, nslots, a.ksplit),
+                       dim3(kDecThreads), lds, s, a);
     return hipGetLastError();
+}
+
+template <int KIND, int DT, int NT, int G>
+static hipError_t launch_decode_ntg(const GemmArgs& a, int nslots, hipStream_t s) {
+    if constexpr (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) {
+        if (a.act_q8) return launch_decode_ntga<KIND, DT, NT, G, true>(a, nslots, s);
+    }
+    return launch_decode_ntga<KIND, DT, NT, G, false>(a, nslots, s);
 }
 
 template <int KIND, int DT, int NT>
@@ -892,9 +904,39 @@ hipError_t launch_grouped_gemm(const GemmCall& c, hipStream_t s) {
     a.c_amax = c.c_amax;
     a.ksplit = c.ksplit;
     a.cpart = c.cpart;
+    a.act_q8 = c.act_q8 ? 1 : 0;
     const int64_t cap = moe_align_capacity(c.M, c.topk, c.E, c.block_m);
     if (c.kind == MOE_GEMM_GATE_UP_SILU) return launch_kind<MOE_GEMM_GATE_UP_SILU>(c, a, cap, s);
     return launch_kind<MOE_GEMM_DOWN>(c, a, cap, s);
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ------------------------------------------------------- fp8 intermediate
+//
+// The fused layer quantises the bf16 intermediate once (value / (amax/448),
+// IEEE division, round to nearest even, as quant8 does on load in the
+// stand-alone down GEMM) so the down GEMM reads e4m3 codes directly.
+// Each thread converts 16 elements.
+__global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restrict__ act,
+                                                        const float* __restrict__ amax, uint8_t* __restrict__ q,
+                                                        size_t n16) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n16) return;
+    const float s = act_scale_from_amax(amax);
+    const uint4* p = reinterpret_cast<const uint4*>(act) + 2 * i;
+    const uint2 lo = quant8(p[0], s), hi = quant8(p[1], s);
+    reinterpret_cast<uint4*>(q)[i] = uint4{lo.x, lo.y, hi.x, hi.y};
+}
+
+hipError_t launch_quant_act(const void* act, const float* amax, void* q, size_t n, hipStream_t s) {
+    const size_t n16 = n / 16;
+    if (n16 == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(act), amax, static_cast<uint8_t*>(q), n16);
+    return hipGetLastError();
 }
 
 }  // namespace moe

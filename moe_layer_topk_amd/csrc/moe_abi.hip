@@ -65,6 +65,7 @@ struct FusedLayout {
     moe_align_bufs al;
     void* act;
     void* y;
+    void* act_q;  // fp8: e4m3 codes of act
     float* ypart;
     float* amax;
 };
@@ -86,6 +87,7 @@ FusedLayout fused_layout(char* ws, moe_dtype dtype, int32_t M, int32_t E, int32_
     L.amax = c.take<float>(1);
     L.act = c.take<char>((size_t)P * I * inter_bytes(dtype));
     L.y = c.take<char>((size_t)P * H * inter_bytes(dtype));
+    L.act_q = dtype == MOE_FP8_E4M3 ? c.take<char>((size_t)P * I) : nullptr;
     L.ksplit = down_ksplit(dtype, M, topk, E, H, I, L.block_m);
     L.ypart = L.ksplit > 1 ? c.take<float>((size_t)L.ksplit * P * H) : nullptr;
     L.bytes = c.off;
@@ -225,8 +227,9 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
     GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, x, x_scale, w1, w1_scale, L.al, M, topk, E, 2 * I, H,
                 L.block_m, L.act, fp8 ? L.amax : nullptr};
     if (launch_grouped_gemm(g1, s) != hipSuccess) return MOE_ERR_HIP;
-    GemmCall g2{MOE_GEMM_DOWN, dtype, L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E, H, I,
-                L.block_m, L.y, nullptr, L.ksplit, L.ypart};
+    if (fp8 && launch_quant_act(L.act, L.amax, L.act_q, (size_t)M * topk * I, s) != hipSuccess) return MOE_ERR_HIP;
+    GemmCall g2{MOE_GEMM_DOWN, dtype, fp8 ? L.act_q : L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E,
+                H, I, L.block_m, L.y, nullptr, L.ksplit, L.ypart, fp8};
     if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
     if (L.ksplit > 1) return hip_status(launch_combine_partials(L.ypart, L.ksplit, wts, M, topk, H, inter, out, s));
     return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));
