@@ -148,27 +148,42 @@ def main():
             return res
         # per-kernel durations through the per-step entry points, events around each launch
         block_m = 128 if (Mc * k) // E > 64 else 16
-        names = ["route", "align", "gate_up", "down", "combine"]
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
-        amax = torch.empty(1, dtype=torch.float32, device=dev) if cfg.dtype == "fp8" else None
+        fp8 = cfg.dtype == "fp8"
+        names = ["route", "align", "gate_up"] + (["quant_act"] if fp8 else []) + ["down", "combine"]
+        nk = len(names)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+        amax = torch.empty(1, dtype=torch.float32, device=dev) if fp8 else None
         act = torch.empty((Mc * k, I), dtype=out.dtype, device=dev)
+        act_q = torch.empty((Mc * k, I), dtype=torch.float8_e4m3fn, device=dev) if fp8 else None
         y = torch.empty((Mc * k, H), dtype=out.dtype, device=dev)
         wts = torch.empty((Mc, k), dtype=torch.float32, device=dev)
 
         def staged(e):
-            if e: e[0].record()
+            i = 0
+            if e: e[i].record()
             moe.moe_route(b["logits"], k, topk_ids=ids, topk_weights=wts)
-            if e: e[1].record()
+            i += 1
+            if e: e[i].record()
             al = moe.moe_align(ids, E, block_m)
-            if e: e[2].record()
+            i += 1
+            if e: e[i].record()
             moe.moe_grouped_gemm(moe.MOE_GEMM_GATE_UP_SILU, b["x"], w["w1"], al, Mc, k, a_scale=b["x_scale"],
                                  w_scale=w["w1_scale"], c=act, c_amax=amax)
-            if e: e[3].record()
-            moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN, act, w["w2"], al, Mc, k, a_scale=amax, w_scale=w["w2_scale"],
-                                 c=y)
-            if e: e[4].record()
+            i += 1
+            if e: e[i].record()
+            if fp8:
+                moe.moe_quant_act(act, amax, out=act_q)
+                i += 1
+                if e: e[i].record()
+                moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN_E4M3_ACT, act_q, w["w2"], al, Mc, k, a_scale=amax,
+                                     w_scale=w["w2_scale"], c=y)
+            else:
+                moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN, act, w["w2"], al, Mc, k, c=y)
+            i += 1
+            if e: e[i].record()
             moe.moe_combine(y, wts, k, out=out)
-            if e: e[5].record()
+            i += 1
+            if e: e[i].record()
 
         for _ in range(warmup):
             staged(None)
@@ -178,12 +193,13 @@ def main():
             staged(ev[s])
         torch.cuda.synchronize()
         res["staged_ms_per_step"] = (time.perf_counter() - t) / steps * 1e3
-        ms = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(5)] for s in range(steps)])
+        ms = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(nk)] for s in range(steps)])
         res["kernel_us"] = {n: float(ms[:, i].mean() * 1e3) for i, n in enumerate(names)}
         gu = gate_up_bytes(cfg, Mc, n_active, wb, wb if cfg.dtype != "f32" else 4)
         res["gate_up_bytes"] = gu
         res["gate_up_GBs"] = gu / (res["kernel_us"]["gate_up"] * 1e-6) / 1e9
-        dn = n_active * H * I * wb + Mc * k * I * 2 + Mc * k * H * 2
+        res["gate_up_flops"] = 4.0 * Mc * k * H * I
+        dn = n_active * H * I * wb + Mc * k * I * (1 if fp8 else 2) + Mc * k * H * 2
         res["down_GBs"] = dn / (res["kernel_us"]["down"] * 1e-6) / 1e9
         return res
 
@@ -210,8 +226,19 @@ def main():
         cpu = {"value": M / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"the full {M}-token batch of the timed workload, once ({el:.2f} s)"}
 
-    gu_us = main_res["kernel_us"]["gate_up"]
-    achieved = main_res["gate_up_bytes"] / (gu_us * 1e-6) / 1e9
+    # roofline of the dominant kernel (gate/up): HBM-bound when its weight
+    # bytes take longer at peak bandwidth than its flops at peak MFMA rate
+    gu_s = main_res["kernel_us"]["gate_up"] * 1e-6
+    mfma_peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    if main_res["gate_up_flops"] / (mfma_peak * 1e12) > main_res["gate_up_bytes"] / (HBM_PEAK_GBS * 1e9):
+        achieved = main_res["gate_up_flops"] / gu_s / 1e12
+        roof = {"bound": "mfma", "kernel": "gate_up grouped GEMM", "achieved": achieved, "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": achieved / mfma_peak}
+    else:
+        achieved = main_res["gate_up_bytes"] / gu_s / 1e9
+        roof = {"bound": "hbm", "kernel": "gate_up grouped GEMM", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS}
+    roof["traffic"] = measured_traffic(cfg.name, M)
     line = {
         "metric": "MoE layer tokens/s; decode HBM GB/s & prefill MFMA TFLOP/s as % of peak",
         "value": main_res["tokens_per_s"],
@@ -227,9 +254,7 @@ def main():
         "data": "synthetic (seeded counter-based normals; random-init weights)",
         "config": {"workload": cfg.name, "M": M, "E": cfg.E, "topk": cfg.topk, "hidden": cfg.H,
                    "intermediate": cfg.I, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gate_up grouped GEMM", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(cfg.name, M)},
+        "roofline": roof,
         "cpu_baseline": cpu,
         "layer": {k2: main_res[k2] for k2 in ("roofline_frac", "layer_hbm_frac", "layer_mfma_frac", "kernel_us",
                                               "staged_ms_per_step", "gate_up_GBs", "down_GBs", "active_experts")},

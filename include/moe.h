@@ -52,7 +52,8 @@ typedef enum {
 
 typedef enum {
     MOE_GEMM_GATE_UP_SILU = 0, /* act[p] = silu(W1[e][0:I] x) * (W1[e][I:2I] x) */
-    MOE_GEMM_DOWN = 1          /* y[p]   = W2[e] act[p]                         */
+    MOE_GEMM_DOWN = 1,         /* y[p]   = W2[e] act[p]                         */
+    MOE_GEMM_DOWN_E4M3_ACT = 2 /* as DOWN, act given as e4m3 codes (moe_quant_act) */
 } moe_gemm_kind;
 
 /* The index system produced by moe_align (all device pointers, int32):
@@ -116,6 +117,10 @@ moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t E
  *         bfloat16, c_amax -> float32 that receives max|act| (zeroed by the
  *         call itself); DOWN: a = act bfloat16, a_scale -> that amax, the act
  *         rows are quantised on load with s = amax/448, c = y bfloat16).
+ *  kind = MOE_GEMM_DOWN_E4M3_ACT (MOE_FP8_E4M3 only): as MOE_GEMM_DOWN, but a
+ *         holds the e4m3 codes [P][K] that moe_quant_act wrote for the same
+ *         amax, and a_scale -> that amax.  The result equals MOE_GEMM_DOWN's
+ *         bit for bit; the act rows are read at one byte per element.
  *  a_scale, w_scale, c_amax must be NULL unless dtype is MOE_FP8_E4M3.
  *  al, block_m: the output of moe_align for the same topk_ids and block_m.
  *  Rows of a expert's run are read through al->sorted_ids; only the first
@@ -126,6 +131,16 @@ moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, 
                             const void* w, const float* w_scale, const moe_align_bufs* al, int32_t M,
                             int32_t topk, int32_t E, int32_t N, int32_t K, int32_t block_m, void* c,
                             float* c_amax, void* stream);
+
+/* Per-tensor e4m3 quantisation of the bfloat16 intermediate, the scaling the
+ * fp8 down projection needs (MoE kernel engineering post, the FP8 part of
+ * its kernel section): s = amax / 448 in float32, code = e4m3 of act / s with
+ * an IEEE float32 division, round to nearest even, saturating at +-448.
+ *  act    device bfloat16 [n]
+ *  amax   device float32 [1], > 0 (as written by the fp8 GATE_UP GEMM)
+ *  act_q  device uint8 [n], e4m3 codes
+ * n must be a multiple of 16 (MOE_ERR_SHAPE otherwise); n = 0 is a no-op. */
+moe_status moe_quant_act(const void* act, const float* amax, int64_t n, void* act_q, void* stream);
 
 /* Weighted combine back into token order (section 3.1 step 4):
  *  out[t][h] = sum_{j=0..topk-1} topk_weights[t][j] * y[t*topk+j][h], j

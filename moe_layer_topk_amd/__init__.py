@@ -7,7 +7,8 @@ kernels; there is no CPU or framework fallback (a missing library raises).
 
 Steps of the layer (FusedMoE vs MegaMoE post, sections 2 and 3.1):
 moe_route -> moe_align -> moe_grouped_gemm (gate/up + SiLU-and-mul, then
-down) -> moe_combine, or all of them in one call with fused_moe.
+down; for e4m3 weights moe_quant_act between the two) -> moe_combine, or all
+of them in one call with fused_moe.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     MOE_F32,
     MOE_FP8_E4M3,
     MOE_GEMM_DOWN,
+    MOE_GEMM_DOWN_E4M3_ACT,
     MOE_GEMM_GATE_UP_SILU,
     AlignBufs,
     MoeError,
@@ -95,6 +97,8 @@ def moe_grouped_gemm(kind: int, a: torch.Tensor, w: torch.Tensor, al: dict, M: i
     dt = moe_dtype(w)
     P = M * topk
     cols = N // 2 if kind == MOE_GEMM_GATE_UP_SILU else N
+    if kind != MOE_GEMM_GATE_UP_SILU and (kind == MOE_GEMM_DOWN_E4M3_ACT) != (a.dtype == torch.float8_e4m3fn):
+        raise ValueError("MOE_GEMM_DOWN_E4M3_ACT takes e4m3 act codes and e4m3 weights; DOWN takes the bf16 act")
     if c is None:
         c = torch.empty((P, cols), dtype=_INTER[dt], device=w.device)
     if dt == MOE_FP8_E4M3 and kind == MOE_GEMM_GATE_UP_SILU and c_amax is None:
@@ -103,6 +107,15 @@ def moe_grouped_gemm(kind: int, a: torch.Tensor, w: torch.Tensor, al: dict, M: i
     check(lib().moe_grouped_gemm(kind, dt, _p(a), _p(a_scale), _p(w), _p(w_scale), ctypes.byref(bufs), M, topk,
                                  E, N, K, al["block_m"], _p(c), _p(c_amax), _stream(w)), "moe_grouped_gemm")
     return c, c_amax
+
+
+def moe_quant_act(act: torch.Tensor, amax: torch.Tensor, out=None):
+    """e4m3 codes (torch.float8_e4m3fn, same shape) of the bfloat16 intermediate with scale amax/448."""
+    if act.dtype != torch.bfloat16:
+        raise ValueError("moe_quant_act takes the bfloat16 intermediate")
+    q = out if out is not None else torch.empty(act.shape, dtype=torch.float8_e4m3fn, device=act.device)
+    check(lib().moe_quant_act(_p(act), _p(amax), act.numel(), _p(q), _stream(act)), "moe_quant_act")
+    return q
 
 
 def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, topk: int, out_dtype=None, out=None):

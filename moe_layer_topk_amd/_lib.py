@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_ALIGNMENT, MOE_ERR_HIP = range(7)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
-MOE_GEMM_GATE_UP_SILU, MOE_GEMM_DOWN = 0, 1
+MOE_GEMM_GATE_UP_SILU, MOE_GEMM_DOWN, MOE_GEMM_DOWN_E4M3_ACT = 0, 1, 2
 
 
 class AlignBufs(ctypes.Structure):
@@ -33,6 +33,7 @@ SIGNATURES = {
     "moe_align": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, AlignBufs, _P]),
     "moe_grouped_gemm": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, ctypes.POINTER(AlignBufs),
                                         _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_quant_act": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
     "moe_combine": (ctypes.c_int, [ctypes.c_int, _P, _P, _I32, _I32, _I32, ctypes.c_int, _P, _P]),
     "fused_moe_workspace_size": (_SZ, [ctypes.c_int, _I32, _I32, _I32, _I32, _I32]),
     "fused_moe": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,

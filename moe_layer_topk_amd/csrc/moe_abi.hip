@@ -152,8 +152,12 @@ moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, 
                             const void* w, const float* w_scale, const moe_align_bufs* al, int32_t M,
                             int32_t topk, int32_t E, int32_t N, int32_t K, int32_t block_m, void* c,
                             float* c_amax, void* stream) {
-    if (kind != MOE_GEMM_GATE_UP_SILU && kind != MOE_GEMM_DOWN) return MOE_ERR_UNSUPPORTED;
+    if (kind != MOE_GEMM_GATE_UP_SILU && kind != MOE_GEMM_DOWN && kind != MOE_GEMM_DOWN_E4M3_ACT)
+        return MOE_ERR_UNSUPPORTED;
     if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if (kind == MOE_GEMM_DOWN_E4M3_ACT && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    const bool act_q8 = kind == MOE_GEMM_DOWN_E4M3_ACT;
+    if (act_q8) kind = MOE_GEMM_DOWN;
     moe_status st = check_router(M, E, topk);
     if (st != MOE_OK) return st;
     if (N < 1 || K < 1 || N % 128 || K % 128) return MOE_ERR_SHAPE;
@@ -168,13 +172,21 @@ moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, 
         return MOE_ERR_NULL;
     if (fp8 && (!a_scale || !w_scale || (kind == MOE_GEMM_GATE_UP_SILU && !c_amax))) return MOE_ERR_NULL;
     if (misaligned(a) || misaligned(w) || misaligned(c)) return MOE_ERR_ALIGNMENT;
-    GemmCall g{kind, dtype, a, a_scale, w, w_scale, *al, M, topk, E, N, K, block_m, c, c_amax};
+    GemmCall g{kind, dtype, a, a_scale, w, w_scale, *al, M, topk, E, N, K, block_m, c, c_amax, 1, nullptr, act_q8};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (fp8 && kind == MOE_GEMM_GATE_UP_SILU) {
         hipError_t e = launch_fill_zero_f32(c_amax, 1, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
     return hip_status(launch_grouped_gemm(g, s));
+}
+
+moe_status moe_quant_act(const void* act, const float* amax, int64_t n, void* act_q, void* stream) {
+    if (n < 0 || n % 16) return MOE_ERR_SHAPE;
+    if (n == 0) return MOE_OK;
+    if (!act || !amax || !act_q) return MOE_ERR_NULL;
+    if (misaligned(act) || misaligned(act_q)) return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_quant_act(act, amax, act_q, (size_t)n, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_combine(moe_dtype y_dtype, const void* y, const float* topk_weights, int32_t M,

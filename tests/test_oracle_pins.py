@@ -350,3 +350,19 @@ def test_fp8_layer_matches_brute_force_with_torch_codec():
     ref = dense_masked(x, w1d, w2d, lg, k, act_fn=q)
     out = oracle.moe_layer("fp8", xq, sx, lg, w1, s1, w2, s2, k, act_amax_value=amax)
     np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+
+
+def test_fp8_golden_amax_single_token_recomputes():
+    """The stored batch amax of the fp8 workload at M=1 is the oracle's (only the
+    8 experts the token is routed to are generated here)."""
+    import json
+    import os
+    from workloads import CONFIGS, layer_batch, layer_weights
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fp8_act_amax.json")))
+    cfg = CONFIGS["fp8_e4m3"]
+    b = layer_batch(cfg, 1, "cpu")
+    assert float(b["x_scale"][0]) == gold["fingerprint"]["1"]["x_scale"]
+    ids, _ = oracle.route(b["logits"], cfg.topk)
+    w = layer_weights(cfg, "cpu", experts=sorted(set(ids.reshape(-1).tolist())))
+    am = oracle.act_amax("fp8", b["x"], b["x_scale"], b["logits"], w["w1"], w["w1_scale"], cfg.topk)
+    assert am == gold["amax"]["1"]

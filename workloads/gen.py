@@ -114,15 +114,20 @@ def normal_bf16(seed, stream, shape, std, device, offset=0) -> torch.Tensor:
 
 
 def _quant_e4m3_per_tensor(v: torch.Tensor):
-    """Store a float32 tensor as OCP e4m3 with one float32 scale = amax/448.
+    """Store a float32 tensor as OCP e4m3 with one float32 scale s = amax/448.
 
-    Uses torch's own float8_e4m3fn cast (round to nearest even); the clamp
-    keeps values that would round past 448 finite.
+    s and 1/s are computed on the host in IEEE float32 (numpy), and the codes
+    are torch's float8_e4m3fn cast (round to nearest even) of v * (1/s), so a
+    CPU and a GPU draw give the same bytes (a division by a scalar is not
+    rounded the same way on both).  The clamp keeps values that would round
+    past 448 finite.
     """
-    amax = v.abs().max()
-    s = amax / 448.0 if float(amax) > 0 else torch.ones((), dtype=torch.float32, device=v.device)
-    q = (v / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
-    return q, s.to(torch.float32).reshape(1)
+    import numpy as np
+    amax = np.float32(v.abs().max().item())
+    s = amax / np.float32(448.0) if amax > 0 else np.float32(1.0)
+    inv = np.float32(1.0) / s
+    q = (v * float(inv)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q, torch.tensor([float(s)], dtype=torch.float32, device=v.device)
 
 
 @dataclass(frozen=True)
