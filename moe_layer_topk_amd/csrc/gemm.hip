@@ -524,8 +524,16 @@ constexpr int kP2GroupN = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// 16 bytes per lane from global memory straight into LDS: the wave's 64
+// lanes fill 1 KB at the wave-uniform LDS address in M0.  Issued through
+// inline asm so the compiler does not treat every later LDS read as
+// dependent on the copy (it would wait for all copies in flight, prefetched
+// stages included); the kernel orders the ring itself with explicit vmcnt
+// waits and barriers.  "memory" keeps LDS reads and writes of the kernel in
+// program order around it.
 __device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
 
 // wait until at most n vector-memory operations of this wave are outstanding
@@ -626,16 +634,21 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
         bsrc[j] = wbase + (size_t)row * rowb + C::swz(lphys, r) * 16;
     }
 
-    auto issue = [&](int kt) {
+    // copy instructions [j0, j1) of stage kt (A rows first, then B rows)
+    auto issue_part = [&](int kt, int j0, int j1) {
         char* st = p2_lds + (kt % C::ST) * C::StageBytes;
         const size_t koff = (size_t)kt * C::RowBytes;
 #pragma unroll
-        for (int j = 0; j < C::ALoads; ++j)
-            lds_dma16(asrc[j] + koff, st + (wave * C::ALoads + j) * C::RowsPerLoad * C::RowBytes);
-#pragma unroll
-        for (int j = 0; j < C::BLoads; ++j)
-            lds_dma16(bsrc[j] + koff, st + C::ABytes + (wave * C::BLoads + j) * C::RowsPerLoad * C::RowBytes);
+        for (int j = 0; j < C::L; ++j) {
+            if (j < j0 || j >= j1) continue;
+            if (j < C::ALoads)
+                lds_dma16(asrc[j] + koff, st + (wave * C::ALoads + j) * C::RowsPerLoad * C::RowBytes);
+            else
+                lds_dma16(bsrc[j - C::ALoads] + koff,
+                          st + C::ABytes + (wave * C::BLoads + (j - C::ALoads)) * C::RowsPerLoad * C::RowBytes);
+        }
     };
+    auto issue = [&](int kt) { issue_part(kt, 0, C::L); };
 
     f32x16 acc[C::TM][C::TN];
 #pragma unroll
@@ -668,7 +681,11 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
         const int ahead = min(C::ST - 2, nk - 1 - kt);  // later stages already issued
         wait_vm_runtime<C::L>(ahead);
         __syncthreads();
-        if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1);
+        // the copies of stage kt + ST - 1 (into the buffer every wave finished
+        // reading before this barrier) are spread over the K substeps, between
+        // MFMA groups, so the wave never stalls on a burst of copies while its
+        // matrix core idles
+        const bool pf = kt + C::ST - 1 < nk;
         const char* st = p2_lds + (kt % C::ST) * C::StageBytes;
         const char* sa = st;
         const char* sb = st + C::ABytes;
@@ -689,12 +706,24 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
         for (int ks = 0; ks < C::BK / 16; ++ks) {
             const int cur = ks & 1;
             if (ks + 1 < C::BK / 16) read_frags(cur ^ 1, ks + 1);
+            // this substep's share of the copies, one after every kGap MFMAs:
+            // a copy is issued while the matrix core works on the MFMA before it
+            constexpr int kPer = (C::L + C::BK / 16 - 1) / (C::BK / 16);
+            constexpr int kGap = (C::TM * C::TN) / kPer > 0 ? (C::TM * C::TN) / kPer : 1;
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+            for (int q = 0; q < C::TM * C::TN; ++q) {
+                const int i = q / C::TN, j = q % C::TN;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+                if ((q + 1) % kGap == 0) {
+                    const int jj = ks * kPer + (q + 1) / kGap - 1;
+                    if (pf && (q + 1) / kGap <= kPer && jj < C::L) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue_part(kt + C::ST - 1, jj, jj + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
