@@ -119,8 +119,10 @@ moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t E
  *         rows are quantised on load with s = amax/448, c = y bfloat16).
  *  kind = MOE_GEMM_DOWN_E4M3_ACT (MOE_FP8_E4M3 only): as MOE_GEMM_DOWN, but a
  *         holds the e4m3 codes [P][K] that moe_quant_act wrote for the same
- *         amax, and a_scale -> that amax.  The result equals MOE_GEMM_DOWN's
- *         bit for bit; the act rows are read at one byte per element.
+ *         amax, and a_scale -> that amax.  The products are those of
+ *         MOE_GEMM_DOWN (same codes, same scales); the act rows are read at
+ *         one byte per element, and a kernel that needs the codes in LDS
+ *         serves the call, so results agree with MOE_GEMM_DOWN to rounding.
  *  a_scale, w_scale, c_amax must be NULL unless dtype is MOE_FP8_E4M3.
  *  al, block_m: the output of moe_align for the same topk_ids and block_m.
  *  Rows of a expert's run are read through al->sorted_ids; only the first

@@ -51,6 +51,21 @@ struct Opnd<MOE_FP8_E4M3> {
     }
 };
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 16x16 tile over 128 e4m3 products per lane group: gfx950's f8f6f4 MFMA
+// (4x the K of v_mfma_f32_16x16x32_fp8_fp8 per instruction, about 3x its
+// throughput).  Each operand is 32 bytes per lane given as two 16-byte
+// halves; the same byte positions of A and B meet in the same product, so
+// any K order works as long as both operands are loaded alike.  Scale
+// operands 0 select the unscaled form.
+__device__ __forceinline__ f32x4 mfma_f8_16x16x128(const uint4& a0, const uint4& a1, const uint4& b0,
+                                                   const uint4& b1, f32x4 c) {
+    const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // 8 bf16 activations quantised to 8 e4m3 codes with value/s (IEEE division).
 __device__ __forceinline__ uint2 quant8(const uint4& v, float s) {
     float f[8];
@@ -245,10 +260,21 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
 #pragma unroll
                 for (int c = 0; c < NT; ++c) {
                     if (c < ntiles) {
+                        if constexpr (DT == MOE_FP8_E4M3) {
+                            // a step's 256 bytes per row: two f8f6f4 MFMAs
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
+                            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                            for (int t = 0; t < T; ++t) acc[gg][t][c] = mfma_chunk<DT>(a0[t][u], b0[c][u], acc[gg][t][c]);
+                                for (int t = 0; t < T; ++t)
+                                    acc[gg][t][c] = mfma_f8_16x16x128(a0[t][2 * h], a0[t][2 * h + 1], b0[c][2 * h],
+                                                                      b0[c][2 * h + 1], acc[gg][t][c]);
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                                for (int t = 0; t < T; ++t)
+                                    acc[gg][t][c] = mfma_chunk<DT>(a0[t][u], b0[c][u], acc[gg][t][c]);
+                        }
                     }
                 }
             }
@@ -332,14 +358,15 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
 
 constexpr int kPreThreads = 256;
 constexpr int kPreBN = 128;  // weight rows per workgroup
-constexpr int kPreBK = 64;   // K elements per stage
+constexpr int kPreBK = 64;   // K elements per stage (bf16; e4m3 stages 128 elements, the same bytes)
 
 template <int KIND, int DT, int BM>
 __global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
     using O = Opnd<DT>;
     using chunk = typename O::chunk;
     constexpr int kElem = O::kElemBytes;
-    constexpr int kRowBytes = kPreBK * kElem;        // bytes of one staged row
+    constexpr int kBK = (DT == MOE_FP8_E4M3) ? 2 * kPreBK : kPreBK;  // K elements per stage
+    constexpr int kRowBytes = kBK * kElem;           // bytes of one staged row
     constexpr int kLdsStride = kRowBytes + 16;       // padded LDS row
     constexpr int kChunksPerRow = kRowBytes / 16;    // 16-byte global chunks per row
     constexpr int kAChunks = BM * kChunksPerRow / kPreThreads;
@@ -444,26 +471,48 @@ __global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
             bcol[j] = wn * 64 + 16 * j;
     }
 
-    const int nk = K / kPreBK;
+    const int nk = K / kBK;
     gload(0);
     sstore();
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) gload((kt + 1) * kPreBK);
-#pragma unroll
-        for (int ks = 0; ks < kPreBK / 32; ++ks) {
-            const int koff = (ks * 32 + lg * 8) * kElem;
-            chunk af[kTM], bf[4];
+        if (kt + 1 < nk) gload((kt + 1) * kBK);
+        if constexpr (DT == MOE_FP8_E4M3) {
+            // the stage's 128 bytes per row: lane group lg takes bytes [32 lg, 32 lg + 32)
+            const int koff = lg * 32;
+            uint4 af[kTM][2], bf[4][2];
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
-                af[i] = *reinterpret_cast<const chunk*>(As + (wm * kWM + 16 * i + lr) * kLdsStride + koff);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    af[i][hh] = *reinterpret_cast<const uint4*>(As + (wm * kWM + 16 * i + lr) * kLdsStride + koff +
+                                                                16 * hh);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const chunk*>(Bs + (bcol[j] + lr) * kLdsStride + koff);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    bf[j][hh] = *reinterpret_cast<const uint4*>(Bs + (bcol[j] + lr) * kLdsStride + koff + 16 * hh);
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = O::mfma(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = mfma_f8_16x16x128(af[i][0], af[i][1], bf[j][0], bf[j][1], acc[i][j]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < kBK / 32; ++ks) {
+                const int koff = (ks * 32 + lg * 8) * kElem;
+                chunk af[kTM], bf[4];
+#pragma unroll
+                for (int i = 0; i < kTM; ++i)
+                    af[i] = *reinterpret_cast<const chunk*>(As + (wm * kWM + 16 * i + lr) * kLdsStride + koff);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bf[j] = *reinterpret_cast<const chunk*>(Bs + (bcol[j] + lr) * kLdsStride + koff);
+#pragma unroll
+                for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = O::mfma(af[i], bf[j], acc[i][j]);
+            }
         }
         __syncthreads();
         if (kt + 1 < nk) {
@@ -579,11 +628,36 @@ struct P2Cfg {
     static_assert(LdsBytes <= 160 * 1024, "LDS");
 };
 
+// 32x32 MFMA on one K substep of the LDS ring.  bf16: 16 K values, one
+// 16-byte chunk per lane; e4m3: 64 K values, two chunks per lane, gfx950's
+// f8f6f4 MFMA with its scale operands at 0 (unscaled form).
+template <int DT>
+struct P2Mfma {
+    static constexpr int kChunks = (DT == MOE_FP8_E4M3) ? 2 : 1;  // 16-byte chunks per lane per substep
+    __device__ static __forceinline__ f32x16 run(const uint4 (&a)[kChunks], const uint4 (&b)[kChunks], f32x16 c) {
+        if constexpr (DT == MOE_FP8_E4M3) {
+            const i32x8 av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                              (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+            const i32x8 bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
+                              (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
+            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+        } else {
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[0]),
+                                                           __builtin_bit_cast(bf16x8_t, b[0]), c, 0, 0, 0);
+        }
+    }
+};
+
 // One wavefront per SIMD (the LDS ring fills the CU): registers are not
-// rationed for occupancy.
-template <int KIND, class C>
+// rationed for occupancy.  A stage holds C::RowBytes bytes of every row
+// (64 bf16 or 128 e4m3 values of K).
+template <int KIND, int DT, class C>
 __global__ void __launch_bounds__(C::Threads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
+    using Mf = P2Mfma<DT>;
+    constexpr int kElem = (DT == MOE_FP8_E4M3) ? 1 : 2;
+    constexpr int kKStage = C::RowBytes / kElem;            // K values per stage
+    constexpr int kSub = C::RowBytes / (16 * Mf::kChunks * 2);  // MFMA K substeps per stage
     extern __shared__ __attribute__((aligned(1024))) char p2_lds[];
     const int nb = m_tiles * n_tiles;
     const int per = (nb + kP2Xcds - 1) / kP2Xcds;
@@ -603,7 +677,7 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to M0
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int K = g.K, N = g.N, I = N / 2, P = g.P;
-    const size_t rowb = (size_t)K * 2;
+    const size_t rowb = (size_t)K * kElem;
     int* ids_s = reinterpret_cast<int*>(p2_lds + C::IdsOffset);
     for (int i = tid; i < C::BM; i += C::Threads) ids_s[i] = g.sorted[mtile * C::BM + i];
 
@@ -671,9 +745,15 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
         else
             brow[j] = wn * C::WTN + 32 * j + (lane & 31);
     }
-    const int khalf = lane >> 5;  // which 8-element half of a 16-wide K slice
+    const int khalf = lane >> 5;  // which half of a K substep this lane holds
 
-    const int nk = K / C::BK;
+    float scale = 1.0f;
+    if constexpr (DT == MOE_FP8_E4M3) {
+        // per-tensor scales: x (GATE_UP) or the intermediate's amax/448 (DOWN)
+        scale = ((KIND == MOE_GEMM_GATE_UP_SILU) ? g.a_scale[0] : act_scale_from_amax(g.a_scale)) * g.w_scale[e];
+    }
+
+    const int nk = K / kKStage;
 #pragma unroll
     for (int s0 = 0; s0 < C::ST - 1; ++s0)
         if (s0 < nk) issue(s0);
@@ -689,32 +769,37 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
         const char* st = p2_lds + (kt % C::ST) * C::StageBytes;
         const char* sa = st;
         const char* sb = st + C::ABytes;
-        // fragments double buffered across the 16-wide K substeps: the reads
-        // for substep ks+1 are interleaved with the MFMAs of substep ks
-        bf16x8_t af[2][C::TM], bfr[2][C::TN];
+        // fragments double buffered across the K substeps: the reads for
+        // substep ks+1 are interleaved with the MFMAs of substep ks.  A lane
+        // takes logical chunks (ks * 2 + khalf) * kChunks + h of its row; the
+        // same chunks of A and B rows meet in the same products
+        uint4 af[2][C::TM][Mf::kChunks], bfr[2][C::TN][Mf::kChunks];
         auto read_frags = [&](int buf, int ks) {
-            const int c = ks * 2 + khalf;  // logical 16-byte chunk
 #pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-                af[buf][i] = *reinterpret_cast<const bf16x8_t*>(sa + arow[i] * C::RowBytes + (C::swz(c, arow[i]) << 4));
+            for (int h = 0; h < Mf::kChunks; ++h) {
+                const int c = (ks * 2 + khalf) * Mf::kChunks + h;  // logical 16-byte chunk
 #pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-                bfr[buf][j] = *reinterpret_cast<const bf16x8_t*>(sb + brow[j] * C::RowBytes + (C::swz(c, brow[j]) << 4));
+                for (int i = 0; i < C::TM; ++i)
+                    af[buf][i][h] = *reinterpret_cast<const uint4*>(sa + arow[i] * C::RowBytes + (C::swz(c, arow[i]) << 4));
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+                    bfr[buf][j][h] = *reinterpret_cast<const uint4*>(sb + brow[j] * C::RowBytes + (C::swz(c, brow[j]) << 4));
+            }
         };
         read_frags(0, 0);
 #pragma unroll
-        for (int ks = 0; ks < C::BK / 16; ++ks) {
+        for (int ks = 0; ks < kSub; ++ks) {
             const int cur = ks & 1;
-            if (ks + 1 < C::BK / 16) read_frags(cur ^ 1, ks + 1);
+            if (ks + 1 < kSub) read_frags(cur ^ 1, ks + 1);
             // this substep's share of the copies, one after every kGap MFMAs:
             // a copy is issued while the matrix core works on the MFMA before it
-            constexpr int kPer = (C::L + C::BK / 16 - 1) / (C::BK / 16);
+            constexpr int kPer = (C::L + kSub - 1) / kSub;
             constexpr int kGap = (C::TM * C::TN) / kPer > 0 ? (C::TM * C::TN) / kPer : 1;
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int q = 0; q < C::TM * C::TN; ++q) {
                 const int i = q / C::TN, j = q % C::TN;
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = Mf::run(af[cur][i], bfr[cur][j], acc[i][j]);
                 if ((q + 1) % kGap == 0) {
                     const int jj = ks * kPer + (q + 1) / kGap - 1;
                     if (pf && (q + 1) / kGap <= kPer && jj < C::L) {
@@ -729,6 +814,7 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
     }
 
     // ---- epilogue: lane holds C[8*(v/4) + 4*(lane/32) + v%4][lane%32] of each 32x32 tile
+    float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
@@ -739,26 +825,34 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
             if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
 #pragma unroll
                 for (int j = 0; j < C::TN / 2; ++j) {
-                    const float gv = acc[i][j][v], uv = acc[i][j + C::TN / 2][v];
+                    float gv = acc[i][j][v], uv = acc[i][j + C::TN / 2][v];
+                    if constexpr (DT == MOE_FP8_E4M3) {
+                        gv *= scale;
+                        uv *= scale;
+                    }
                     const int n = n0 + wn * (C::WTN / 2) + 32 * j + (lane & 31);
-                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * I + n] = f2bf(silu(gv) * uv);
+                    const uint16_t h = f2bf(silu(gv) * uv);
+                    if constexpr (DT == MOE_FP8_E4M3) amax = fmaxf(amax, fabsf(bf2f(h)));
+                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * I + n] = h;
                 }
             } else {
 #pragma unroll
                 for (int j = 0; j < C::TN; ++j) {
                     const int n = n0 + wn * C::WTN + 32 * j + (lane & 31);
-                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * N + n] = f2bf(acc[i][j][v]);
+                    const float y = (DT == MOE_FP8_E4M3) ? acc[i][j][v] * scale : acc[i][j][v];
+                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * N + n] = f2bf(y);
                 }
             }
         }
     }
+    if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) amax_publish(amax, g.c_amax);
 }
 
 // block shape of the LDS-ring prefill kernel
 using PrefillCfg = P2Cfg<128, 256, 64, 3>;
 constexpr int kP2BM = PrefillCfg::BM;
 
-template <int KIND>
+template <int KIND, int DT>
 static hipError_t launch_prefill2(const GemmArgs& a, int64_t cap, hipStream_t s) {
     using C = PrefillCfg;
     const int m_tiles = (int)(cap / C::BM);
@@ -767,10 +861,10 @@ static hipError_t launch_prefill2(const GemmArgs& a, int64_t cap, hipStream_t s)
     const int grid = (nb + kP2Xcds - 1) / kP2Xcds * kP2Xcds;
     // LDS above the default dynamic limit must be requested once per kernel
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_prefill2_kernel<KIND, C>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        reinterpret_cast<const void*>(&gemm_prefill2_kernel<KIND, DT, C>), hipFuncAttributeMaxDynamicSharedMemorySize,
         C::LdsBytes);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemm_prefill2_kernel<KIND, C>), dim3(grid), dim3(C::Threads), C::LdsBytes, s, a, m_tiles,
+    hipLaunchKernelGGL((gemm_prefill2_kernel<KIND, DT, C>), dim3(grid), dim3(C::Threads), C::LdsBytes, s, a, m_tiles,
                        n_tiles);
     return hipGetLastError();
 }
@@ -837,7 +931,11 @@ GemmPath choose_gemm_path(const GemmCall& g) {
     if (env && strcmp(env, "prefill") == 0 && pre_ok) return GemmPath::kPrefill;
     const long P = (long)g.M * g.topk;
     const long per_expert = P / g.E;
-    return (per_expert > 64 && pre_ok) ? GemmPath::kPrefill : GemmPath::kDecode;
+    // e4m3 products cost a quarter of bf16's per byte on the f8f6f4 MFMA, so
+    // the tile kernel (weights read once per 128-row tile) wins from fewer
+    // pairs per expert than for bf16
+    const long min_rows = (g.dtype == MOE_FP8_E4M3) ? 32 : 64;
+    return (per_expert > min_rows && pre_ok) ? GemmPath::kPrefill : GemmPath::kDecode;
 }
 
 template <int KIND, int DT, int NT, int G, bool AQ>
@@ -902,12 +1000,16 @@ static hipError_t launch_kind(const GemmCall& c, const GemmArgs& a, int64_t cap,
         return hipGetLastError();
     }
     const GemmPath path = choose_gemm_path(c);
+    const int n2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? (c.N / 2) % (PrefillCfg::BN / 2) : c.N % PrefillCfg::BN;
+    const bool ring = path == GemmPath::kPrefill && c.block_m == kP2BM && n2 == 0;
     if (c.dtype == MOE_BF16) {
-        const int n2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? (c.N / 2) % (PrefillCfg::BN / 2) : c.N % PrefillCfg::BN;
-        if (path == GemmPath::kPrefill && c.block_m == kP2BM && n2 == 0) return launch_prefill2<KIND>(a, cap, s);
+        if (ring) return launch_prefill2<KIND, MOE_BF16>(a, cap, s);
         if (path == GemmPath::kPrefill) return launch_prefill<KIND, MOE_BF16>(a, c.block_m, cap, s);
         return launch_decode<KIND, MOE_BF16>(a, c.M, c.topk, c.E, s);
     }
+    // the ring kernel reads e4m3 rows only: a bf16 intermediate (DOWN without
+    // act_q8) is quantised on load by the register-staged kernels
+    if (ring && (KIND == MOE_GEMM_GATE_UP_SILU || c.act_q8)) return launch_prefill2<KIND, MOE_FP8_E4M3>(a, cap, s);
     if (path == GemmPath::kPrefill) return launch_prefill<KIND, MOE_FP8_E4M3>(a, c.block_m, cap, s);
     return launch_decode<KIND, MOE_FP8_E4M3>(a, c.M, c.topk, c.E, s);
 }

@@ -41,7 +41,7 @@ int32_t fused_block_m(moe_dtype dtype, int32_t M, int32_t E, int32_t topk) {
     if (env && strcmp(env, "prefill") == 0) return 64;
     if (env && strcmp(env, "decode") == 0) return 16;
     const int64_t P = (int64_t)M * topk;
-    return (P / E > 64) ? 128 : 16;
+    return (P / E > ((dtype == MOE_FP8_E4M3) ? 32 : 64)) ? 128 : 16;
 }
 
 struct Carve {

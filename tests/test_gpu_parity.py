@@ -177,7 +177,12 @@ def test_grouped_gemm(dev, monkeypatch, dtype, E, k, H, I, M, path):
         y8, _ = moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN_E4M3_ACT, q, w["w2"].to(dev), al, M, k, a_scale=a_amax,
                                      w_scale=sc(w["w2_scale"]))
         torch.cuda.synchronize()
-        assert torch.equal(y8, y)
+        err8 = rel_err(y8, yref)
+        say(f"  down (e4m3 act) rel err {err8:.2e}")
+        assert err8 <= TOL[dtype]
+        if path == "decode":
+            # the same kernel quantises on load or reads the codes: identical sums
+            assert torch.equal(y8, y)
 
 
 # ----------------------------------------------------------------- combine
