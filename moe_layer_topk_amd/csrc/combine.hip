@@ -16,6 +16,28 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ y
     const int h = (blockIdx.y * 256 + threadIdx.x) * 8;
     if (h >= H) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (YDT == MOE_BF16) {
+        // all k rows' loads are issued before the first use (one memory
+        // latency per thread, not k); the sum still runs j ascending
+        uint4 v[kMaxTopk];
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j)
+            if (j < topk)
+                v[j] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y) +
+                                                       ((size_t)t * topk + j) * H + h);
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j) {
+            if (j < topk) {
+                const float wj = w[(size_t)t * topk + j];
+                const uint32_t q[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = fmaf(wj, __uint_as_float(q[i] << 16), acc[2 * i]);
+                    acc[2 * i + 1] = fmaf(wj, __uint_as_float(q[i] & 0xffff0000u), acc[2 * i + 1]);
+                }
+            }
+        }
+    } else
     for (int j = 0; j < topk; ++j) {
         const float wj = w[(size_t)t * topk + j];
         const size_t row = (size_t)t * topk + j;
@@ -82,12 +104,23 @@ __global__ void __launch_bounds__(256) combine_partials_kernel(const float* __re
     for (int j = 0; j < topk; ++j) {
         const float wj = w[(size_t)t * topk + j];
         const float* row = ypart + ((size_t)t * topk + j) * H + h;
+        // the ksplit partial loads of a row are issued together, then summed z ascending
+        float4 a[kMaxKsplit], b[kMaxKsplit];
+#pragma unroll
+        for (int z = 0; z < kMaxKsplit; ++z) {
+            if (z < ksplit) {
+                const float4* p = reinterpret_cast<const float4*>(row + z * zstride);
+                a[z] = p[0];
+                b[z] = p[1];
+            }
+        }
         float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int z = 0; z < ksplit; ++z) {
-            const float4* p = reinterpret_cast<const float4*>(row + z * zstride);
-            const float4 a = p[0], b = p[1];
-            y[0] += a.x; y[1] += a.y; y[2] += a.z; y[3] += a.w;
-            y[4] += b.x; y[5] += b.y; y[6] += b.z; y[7] += b.w;
+#pragma unroll
+        for (int z = 0; z < kMaxKsplit; ++z) {
+            if (z < ksplit) {
+                y[0] += a[z].x; y[1] += a[z].y; y[2] += a[z].z; y[3] += a[z].w;
+                y[4] += b[z].x; y[5] += b[z].y; y[6] += b[z].z; y[7] += b[z].w;
+            }
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, y[i], acc[i]);

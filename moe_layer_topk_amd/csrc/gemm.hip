@@ -919,7 +919,7 @@ int down_ksplit(moe_dtype dtype, int M, int topk, int E, int N, int K, int block
     if (wgs >= 512) return 1;
     const int steps = (int)((long)K * (dtype == MOE_BF16 ? 2 : 1) / kDecSpan);
     int ks = (int)((768 + wgs - 1) / wgs);
-    if (ks > 8) ks = 8;
+    if (ks > kMaxKsplit) ks = kMaxKsplit;
     if (ks > steps) ks = steps;
     return ks < 1 ? 1 : ks;
 }

@@ -11,8 +11,6 @@ using namespace moe;
 
 namespace {
 
-constexpr int kMaxExperts = 256;
-constexpr int kMaxTopk = 16;
 constexpr int64_t kMaxPairs = 1 << 24;
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -232,9 +230,15 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;
     float* wts = topk_weights_out ? topk_weights_out : L.wts;
-    if (launch_route(router_logits, M, E, topk, renormalize, ids, wts, s) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_align(ids, M, topk, E, L.block_m, L.cap, L.al, fp8 ? L.amax : nullptr, s) != hipSuccess)
-        return MOE_ERR_HIP;
+    if (route_align_fits(M)) {
+        if (launch_route_align(router_logits, M, E, topk, renormalize, ids, wts, L.block_m, L.cap, L.al,
+                               fp8 ? L.amax : nullptr, s) != hipSuccess)
+            return MOE_ERR_HIP;
+    } else {
+        if (launch_route(router_logits, M, E, topk, renormalize, ids, wts, s) != hipSuccess) return MOE_ERR_HIP;
+        if (launch_align(ids, M, topk, E, L.block_m, L.cap, L.al, fp8 ? L.amax : nullptr, s) != hipSuccess)
+            return MOE_ERR_HIP;
+    }
     const moe_dtype inter = dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
     GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, x, x_scale, w1, w1_scale, L.al, M, topk, E, 2 * I, H,
                 L.block_m, L.act, fp8 ? L.amax : nullptr};

@@ -9,6 +9,11 @@
 
 namespace moe {
 
+// Limits the ABI enforces (the kernels size LDS tables and unrolled loops by them).
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopk = 16;
+constexpr int kMaxKsplit = 8;  // K split of the decode DOWN GEMM (float32 partials)
+
 // Which grouped-GEMM kernel family serves a call.
 enum class GemmPath { kAuto = 0, kDecode = 1, kPrefill = 2 };
 
@@ -17,6 +22,12 @@ hipError_t launch_route(const float* logits, int M, int E, int topk, int renorma
 
 hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m, int64_t cap,
                         const moe_align_bufs& out, float* zero_f32, hipStream_t s);
+
+// Both steps in one launch for M <= 16 (one wavefront routes each token).
+bool route_align_fits(int M);
+hipError_t launch_route_align(const float* logits, int M, int E, int topk, int renormalize, int32_t* ids,
+                              float* weights, int block_m, int64_t cap, const moe_align_bufs& out,
+                              float* zero_f32, hipStream_t s);
 
 hipError_t launch_fill_zero_f32(float* p, int n, hipStream_t s);
 

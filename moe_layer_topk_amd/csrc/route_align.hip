@@ -250,6 +250,47 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(
                active, num_active);
 }
 
+// Small batches (M <= 16): one launch for both steps.  Wavefront w routes
+// token w (the same code as route_kernel), the ids go to LDS and to the
+// outputs, and after a barrier the workgroup aligns them.  Saves a launch and
+// the dependency gap between the two, which dominate at a few tokens.
+constexpr int kRouteAlignMaxM = kAlignWaves;
+
+__global__ void __launch_bounds__(kAlignThreads) route_align_kernel(
+    const float* __restrict__ logits, int M, int E, int topk, int renormalize, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int block_m, int cap, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ counts_out, int32_t* __restrict__ offsets_out,
+    int32_t* __restrict__ active, int32_t* __restrict__ num_active, float* __restrict__ zero_f32) {
+    __shared__ int ids_s[kRouteAlignMaxM * kMaxTopk];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0 && zero_f32) *zero_f32 = 0.0f;
+    if (wave < M) {
+        int sel;
+        float w;
+        route_token(logits + (size_t)wave * E, E, topk, renormalize, &sel, &w);
+        if (lane < topk) {
+            ids[(size_t)wave * topk + lane] = sel;
+            weights[(size_t)wave * topk + lane] = w;
+            ids_s[wave * topk + lane] = sel;
+        }
+    }
+    __syncthreads();
+    align_core([&](int p) { return ids_s[p]; }, M * topk, E, block_m, cap, sorted, tile_expert, counts_out,
+               offsets_out, active, num_active);
+}
+
+bool route_align_fits(int M) { return M > 0 && M <= kRouteAlignMaxM; }
+
+hipError_t launch_route_align(const float* logits, int M, int E, int topk, int renormalize, int32_t* ids,
+                              float* weights, int block_m, int64_t cap, const moe_align_bufs& out,
+                              float* zero_f32, hipStream_t s) {
+    if (!route_align_fits(M)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_align_kernel, dim3(1), dim3(kAlignThreads), 0, s, logits, M, E, topk, renormalize, ids,
+                       weights, block_m, (int)cap, out.sorted_ids, out.tile_expert, out.expert_counts,
+                       out.expert_offsets, out.active_experts, out.num_active, zero_f32);
+    return hipGetLastError();
+}
+
 hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m, int64_t cap,
                         const moe_align_bufs& out, float* zero_f32, hipStream_t s) {
     if (M == 0) return hipSuccess;
