@@ -43,13 +43,15 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: measured counter traffic is only reported for the build it was taken on."""
-    import glob
+    """Hash of the sources the grouped-GEMM kernels are built from: measured counter traffic of the
+    gate/up launch is only reported for the kernel code it was taken on."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "moe_layer_topk_amd", "csrc", "*"))):
+    for f in (os.path.join(ROOT, "moe_layer_topk_amd", "csrc", n) for n in ("gemm.hip", "moe_device.h", "moe_launch.h")):
         with open(f, "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "moe.h"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -104,21 +104,28 @@ hipError_t launch_route(const float* logits, int M, int E, int topk, int renorma
 
 // ------------------------------------------------------------------ align
 //
-// One workgroup of 1024 threads.  Counting sort with a stable scatter:
-//  1. LDS histogram of expert ids.
+// min(ceil(P / 1024), 64) workgroups of 1024 threads, no inter-workgroup
+// traffic.  Counting sort with a stable scatter; workgroup b scatters the
+// pairs [b C, b C + C) (C = 1024 up to 64 K pairs):
+//  1. Every workgroup histograms all P expert ids, and separately the ids
+//     before its own chunk, in per-wavefront LDS counters (summed after),
+//     so it knows each expert's count and how many of the expert's pairs
+//     precede its chunk.  (P ids are read by every workgroup: a few KB
+//     to 64 KB from L2, cheaper than a second launch.)
 //  2. Padded exclusive scan over experts (one wavefront, shuffles).
-//  3. Every position of sorted_ids past the real rows of its run gets the
-//     sentinel; tile_expert by binary search over the offsets.
-//  4. Pairs are scattered in chunks of 1024 in p order.  Inside a
-//     wavefront, lanes with the same expert are found with eight ballots
-//     (one per bit of the id) and ranked by popcount below the lane; the
-//     per-wavefront counts are prefix-summed across the 16 wavefronts
-//     through LDS, and a per-expert cursor carries over between chunks.
+//     Workgroup 0 writes the counts, offsets and the active-expert list.
+//  3. Sentinels and the tile map for this workgroup's share of the rows,
+//     tile experts by binary search over the offsets.
+//  4. Stable scatter of the chunk: inside a wavefront, lanes with the same
+//     expert are found with eight ballots (one per bit of the id) and ranked
+//     by popcount below the lane; per-wavefront counts are prefix-summed
+//     across the 16 wavefronts through LDS.
 //  Every write position is a function of topk_ids alone.
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
-constexpr int kMaxE = 256;
+constexpr int kMaxE = kMaxExperts;
+constexpr int kAlignMaxBlocks = 64;
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
     const int lane = __lane_id();
@@ -131,23 +138,44 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 }
 
 template <typename GetId>
-__device__ __forceinline__ void align_core(GetId get_id, int P, int E, int block_m, int cap,
+__device__ __forceinline__ void align_core(GetId get_id, int P, int E, int block_m, int cap, int blk, int nblk,
+                                           int chunk,
                                            int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
                                            int32_t* __restrict__ counts_out, int32_t* __restrict__ offsets_out,
                                            int32_t* __restrict__ active, int32_t* __restrict__ num_active) {
     __shared__ int cnt[kMaxE];
+    __shared__ int before[kMaxE];
     __shared__ int off[kMaxE + 1];
     __shared__ int cursor[kMaxE];
     __shared__ int wcnt[kAlignWaves][kMaxE];
+    __shared__ int wbef[kAlignWaves][kMaxE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    for (int e = tid; e < kMaxE; e += kAlignThreads) cnt[e] = 0;
+    const int chunk0 = blk * chunk;
+    for (int i = tid; i < kAlignWaves * kMaxE; i += kAlignThreads) {
+        (&wcnt[0][0])[i] = 0;
+        (&wbef[0][0])[i] = 0;
+    }
     __syncthreads();
     for (int p = tid; p < P; p += kAlignThreads) {
-        int e = get_id(p);
-        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+        const int e = get_id(p);
+        if ((unsigned)e < (unsigned)E) {
+            atomicAdd(&wcnt[wave][e], 1);
+            if (p < chunk0) atomicAdd(&wbef[wave][e], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < kMaxE; e += kAlignThreads) {
+        int c = 0, b = 0;
+#pragma unroll
+        for (int w = 0; w < kAlignWaves; ++w) {
+            c += wcnt[w][e];
+            b += wbef[w][e];
+        }
+        cnt[e] = c;
+        before[e] = b;
     }
     __syncthreads();
 
@@ -174,26 +202,35 @@ __device__ __forceinline__ void align_core(GetId get_id, int P, int E, int block
             int e = 4 * lane + q;
             if (e < E) {
                 off[e] = run;
-                cursor[e] = run;
-                offsets_out[e] = run;
-                counts_out[e] = c[q];
-                if (act[q]) active[arun] = e;
+                cursor[e] = run + before[e];
+                if (blk == 0) {
+                    offsets_out[e] = run;
+                    counts_out[e] = c[q];
+                    if (act[q]) active[arun] = e;
+                }
             }
             run += pc[q];
             arun += act[q];
         }
         if (lane == 63) {
             off[E] = run;  // E <= 256 so 4*64 covers every expert
-            offsets_out[E] = run;
-            *num_active = nact_total;
+            if (blk == 0) {
+                offsets_out[E] = run;
+                *num_active = nact_total;
+            }
         }
-        for (int i = nact_total + lane; i < amax; i += 64) active[i] = -1;
+        if (blk == 0)
+            for (int i = nact_total + lane; i < amax; i += 64) active[i] = -1;
     }
     __syncthreads();
 
     const int total = off[E];
-    // sentinels and tile map: every row r that is not a real row of a run
-    for (int r = tid; r < cap; r += kAlignThreads) {
+    // sentinels and tile map for rows [r0, r1): every row that is not a real
+    // row of a run gets P; tiles are block_m-aligned so each tile belongs to
+    // exactly one workgroup's row range
+    const int tiles = cap / block_m;
+    const int r0 = (int)((long)tiles * blk / nblk) * block_m, r1 = (int)((long)tiles * (blk + 1) / nblk) * block_m;
+    for (int r = r0 + tid; r < r1; r += kAlignThreads) {
         int e = -1;
         if (r < total) {
             int lo = 0, hi = E - 1;  // last e with off[e] <= r
@@ -209,12 +246,14 @@ __device__ __forceinline__ void align_core(GetId get_id, int P, int E, int block
         if (r % block_m == 0) tile_expert[r / block_m] = e;
     }
 
-    // stable scatter, 1024 pairs per chunk
-    for (int base = 0; base < P; base += kAlignThreads) {
+    // stable scatter of this workgroup's pairs, 1024 at a time; the
+    // per-expert cursor carries over between sub-chunks
+    const int chunk1 = min(P, chunk0 + chunk);
+    for (int base = chunk0; base < chunk1; base += kAlignThreads) {
         for (int i = tid; i < kAlignWaves * kMaxE; i += kAlignThreads) (&wcnt[0][0])[i] = 0;
         __syncthreads();
         const int p = base + tid;
-        int e = (p < P) ? get_id(p) : -1;
+        const int e = (p < chunk1) ? get_id(p) : -1;
         const bool valid = (unsigned)e < (unsigned)E;
         uint64_t same = __ballot(valid);
 #pragma unroll
@@ -244,10 +283,25 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(
     const int32_t* __restrict__ ids, int P, int E, int block_m, int cap, int32_t* __restrict__ sorted,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ counts_out,
     int32_t* __restrict__ offsets_out, int32_t* __restrict__ active, int32_t* __restrict__ num_active,
-    float* __restrict__ zero_f32) {
-    if (threadIdx.x == 0 && zero_f32) *zero_f32 = 0.0f;
-    align_core([&](int p) { return ids[p]; }, P, E, block_m, cap, sorted, tile_expert, counts_out, offsets_out,
-               active, num_active);
+    float* __restrict__ zero_f32, int chunk) {
+    if (blockIdx.x == 0 && threadIdx.x == 0 && zero_f32) *zero_f32 = 0.0f;
+    align_core([&](int p) { return ids[p]; }, P, E, block_m, cap, blockIdx.x, gridDim.x, chunk, sorted, tile_expert,
+               counts_out, offsets_out, active, num_active);
+}
+
+hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m, int64_t cap,
+                        const moe_align_bufs& out, float* zero_f32, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const int P = M * topk;
+    // every workgroup reads all P ids, so their number is capped: past 64 K
+    // pairs a workgroup scatters several 1024-pair sub-chunks
+    const int units = (P + kAlignThreads - 1) / kAlignThreads;
+    const int nblk = units < kAlignMaxBlocks ? units : kAlignMaxBlocks;
+    const int chunk = (units + nblk - 1) / nblk * kAlignThreads;
+    hipLaunchKernelGGL(align_kernel, dim3(nblk), dim3(kAlignThreads), 0, s, ids, P, E, block_m, (int)cap,
+                       out.sorted_ids, out.tile_expert, out.expert_counts, out.expert_offsets, out.active_experts,
+                       out.num_active, zero_f32, chunk);
+    return hipGetLastError();
 }
 
 // Small batches (M <= 16): one launch for both steps.  Wavefront w routes
@@ -275,7 +329,8 @@ __global__ void __launch_bounds__(kAlignThreads) route_align_kernel(
         }
     }
     __syncthreads();
-    align_core([&](int p) { return ids_s[p]; }, M * topk, E, block_m, cap, sorted, tile_expert, counts_out,
+    align_core([&](int p) { return ids_s[p]; }, M * topk, E, block_m, cap, 0, 1, kAlignThreads, sorted, tile_expert,
+               counts_out,
                offsets_out, active, num_active);
 }
 
@@ -287,15 +342,6 @@ hipError_t launch_route_align(const float* logits, int M, int E, int topk, int r
     if (!route_align_fits(M)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(route_align_kernel, dim3(1), dim3(kAlignThreads), 0, s, logits, M, E, topk, renormalize, ids,
                        weights, block_m, (int)cap, out.sorted_ids, out.tile_expert, out.expert_counts,
-                       out.expert_offsets, out.active_experts, out.num_active, zero_f32);
-    return hipGetLastError();
-}
-
-hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m, int64_t cap,
-                        const moe_align_bufs& out, float* zero_f32, hipStream_t s) {
-    if (M == 0) return hipSuccess;
-    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, M * topk, E, block_m,
-                       (int)cap, out.sorted_ids, out.tile_expert, out.expert_counts,
                        out.expert_offsets, out.active_experts, out.num_active, zero_f32);
     return hipGetLastError();
 }

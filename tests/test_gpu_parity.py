@@ -90,7 +90,10 @@ def _check_align(got, ref):
 
 ALIGN_CASES = [("uniform", 64, 8, 2), ("uniform", 4096, 8, 2), ("zipf", 4096, 8, 2), ("uniform", 2048, 128, 8),
                ("uniform", 512, 64, 8), ("uniform", 1, 8, 2), ("one_expert", 300, 8, 1), ("two_experts", 96, 128, 2),
-               ("divisible", 128, 8, 2), ("uniform", 16, 128, 8), ("uniform", 5000, 256, 4)]
+               ("divisible", 128, 8, 2), ("uniform", 16, 128, 8), ("uniform", 5000, 256, 4),
+               # 72000 pairs: more 1024-pair units than workgroups, so workgroups scatter two units and the
+               # last ones only write sentinels and tile entries
+               ("uniform", 9000, 128, 8), ("zipf", 40000, 8, 2)]
 
 
 @pytest.mark.parametrize("kind,M,E,k", ALIGN_CASES)
