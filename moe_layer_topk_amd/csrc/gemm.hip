@@ -42,6 +42,12 @@ struct Opnd<MOE_BF16> {
 };
 
 template <>
+struct Opnd<MOE_F32> {
+    using chunk = uint4;  // 4 float32
+    static constexpr int kElemBytes = 4;
+};
+
+template <>
 struct Opnd<MOE_FP8_E4M3> {
     using chunk = uint2;  // 8 e4m3
     static constexpr int kElemBytes = 1;
@@ -149,6 +155,13 @@ template <int DT>
 __device__ __forceinline__ f32x4 mfma_chunk(const uint4& a, const uint4& b, f32x4 c) {
     if constexpr (DT == MOE_BF16) {
         return Opnd<MOE_BF16>::mfma(a, b, c);
+    } else if constexpr (DT == MOE_F32) {
+        // 16x16x4 f32: one float per lane and operand; float i of the lane's
+        // chunk goes to the i-th MFMA for A and B alike
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
     } else {
         c = Opnd<MOE_FP8_E4M3>::mfma(uint2{a.x, a.y}, uint2{b.x, b.y}, c);
         return Opnd<MOE_FP8_E4M3>::mfma(uint2{a.z, a.w}, uint2{b.z, b.w}, c);
@@ -314,7 +327,14 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
                     gs += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
                     us += red[((w * G * T + gi * T + q + 2) * NT + c) * 64 + lane];
                 }
-                if (r < cnt) {
+                if (r < cnt && DT == MOE_F32) {
+                    const int p = g.sorted[base + r];
+                    f32x4 o;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[v] = silu(gs[v]) * us[v];
+                    const int n = n0 + gi * 32 + 16 * q + 4 * lg;
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.c) + (size_t)p * I + n) = o;
+                } else if (r < cnt) {
                     const int p = g.sorted[base + r];
                     float o[4];
 #pragma unroll
@@ -335,7 +355,11 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
                 f32x4 ys = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int w = 0; w < 4; ++w) ys += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
-                if (r < cnt && g.cpart) {
+                if (r < cnt && DT == MOE_F32) {
+                    const int p = g.sorted[base + r];
+                    const int n = n0 + gi * 64 + 16 * q + 4 * lg;
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.c) + (size_t)p * N + n) = ys;
+                } else if (r < cnt && g.cpart) {
                     const int p = g.sorted[base + r];
                     const int n = n0 + gi * 64 + 16 * q + 4 * lg;
                     *reinterpret_cast<f32x4*>(g.cpart + ((size_t)blockIdx.z * g.P + p) * N + n) = ys * scale;
@@ -993,6 +1017,8 @@ static hipError_t launch_prefill(const GemmArgs& a, int block_m, int64_t cap, hi
 
 template <int KIND>
 static hipError_t launch_kind(const GemmCall& c, const GemmArgs& a, int64_t cap, hipStream_t s) {
+    if (c.dtype == MOE_F32 && choose_gemm_path(c) == GemmPath::kDecode)
+        return launch_decode<KIND, MOE_F32>(a, c.M, c.topk, c.E, s);
     if (c.dtype == MOE_F32) {
         const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? c.N / 2 : c.N;
         dim3 grid((unsigned)((cap + 3) / 4), (ncols + 63) / 64);
