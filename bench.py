@@ -149,8 +149,9 @@ def main():
         if not events:
             return res
         # per-kernel durations through the per-step entry points, events around each launch
-        # the tile height fused_moe picks (weights read once per 128-row tile above this many pairs per expert)
-        block_m = 128 if (Mc * k) // E > (32 if cfg.dtype == "fp8" else 64) else 16
+        # the tile height fused_moe picks for this batch
+        pe = (Mc * k) // E
+        block_m = 128 if pe > (32 if cfg.dtype == "fp8" else 64) else 16
         fp8 = cfg.dtype == "fp8"
         names = ["route", "align", "gate_up"] + (["quant_act"] if fp8 else []) + ["down", "combine"]
         nk = len(names)

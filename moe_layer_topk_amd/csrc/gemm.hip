@@ -833,6 +833,12 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
                     }
                 }
             }
+            // a substep with fewer MFMAs than copies issues the rest here
+            constexpr int kInLoop = (C::TM * C::TN) / kGap < kPer ? (C::TM * C::TN) / kGap : kPer;
+            if (pf && kInLoop < kPer) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue_part(kt + C::ST - 1, ks * kPer + kInLoop, min(C::L, (ks + 1) * kPer));
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -872,13 +878,14 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles) {
     if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) amax_publish(amax, g.c_amax);
 }
 
-// block shape of the LDS-ring prefill kernel
+// block shapes of the LDS-ring prefill kernel: 128-row tiles (what the fused
+// layer uses), and 64-row tiles for callers that align with block_m = 64
 using PrefillCfg = P2Cfg<128, 256, 64, 3>;
-constexpr int kP2BM = PrefillCfg::BM;
+using PrefillCfg64 = P2Cfg<64, 256, 64, 3>;
+static_assert(PrefillCfg::BN == PrefillCfg64::BN, "one weight-tile width");
 
-template <int KIND, int DT>
+template <int KIND, int DT, class C>
 static hipError_t launch_prefill2(const GemmArgs& a, int64_t cap, hipStream_t s) {
-    using C = PrefillCfg;
     const int m_tiles = (int)(cap / C::BM);
     const int n_tiles = (KIND == MOE_GEMM_GATE_UP_SILU) ? (a.N / 2) / (C::BN / 2) : a.N / C::BN;
     const int nb = m_tiles * n_tiles;
@@ -1027,15 +1034,20 @@ static hipError_t launch_kind(const GemmCall& c, const GemmArgs& a, int64_t cap,
     }
     const GemmPath path = choose_gemm_path(c);
     const int n2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? (c.N / 2) % (PrefillCfg::BN / 2) : c.N % PrefillCfg::BN;
-    const bool ring = path == GemmPath::kPrefill && c.block_m == kP2BM && n2 == 0;
+    const bool ring = path == GemmPath::kPrefill && (c.block_m == PrefillCfg::BM || c.block_m == PrefillCfg64::BM) &&
+                      n2 == 0;
     if (c.dtype == MOE_BF16) {
-        if (ring) return launch_prefill2<KIND, MOE_BF16>(a, cap, s);
+        if (ring && c.block_m == PrefillCfg::BM) return launch_prefill2<KIND, MOE_BF16, PrefillCfg>(a, cap, s);
+        if (ring) return launch_prefill2<KIND, MOE_BF16, PrefillCfg64>(a, cap, s);
         if (path == GemmPath::kPrefill) return launch_prefill<KIND, MOE_BF16>(a, c.block_m, cap, s);
         return launch_decode<KIND, MOE_BF16>(a, c.M, c.topk, c.E, s);
     }
     // the ring kernel reads e4m3 rows only: a bf16 intermediate (DOWN without
     // act_q8) is quantised on load by the register-staged kernels
-    if (ring && (KIND == MOE_GEMM_GATE_UP_SILU || c.act_q8)) return launch_prefill2<KIND, MOE_FP8_E4M3>(a, cap, s);
+    if (ring && (KIND == MOE_GEMM_GATE_UP_SILU || c.act_q8)) {
+        if (c.block_m == PrefillCfg::BM) return launch_prefill2<KIND, MOE_FP8_E4M3, PrefillCfg>(a, cap, s);
+        return launch_prefill2<KIND, MOE_FP8_E4M3, PrefillCfg64>(a, cap, s);
+    }
     if (path == GemmPath::kPrefill) return launch_prefill<KIND, MOE_FP8_E4M3>(a, c.block_m, cap, s);
     return launch_decode<KIND, MOE_FP8_E4M3>(a, c.M, c.topk, c.E, s);
 }

@@ -38,8 +38,10 @@ int32_t fused_block_m(moe_dtype dtype, int32_t M, int32_t E, int32_t topk) {
     const char* env = getenv("MOE_GEMM_PATH");
     if (env && strcmp(env, "prefill") == 0) return 64;
     if (env && strcmp(env, "decode") == 0) return 16;
-    const int64_t P = (int64_t)M * topk;
-    return (P / E > ((dtype == MOE_FP8_E4M3) ? 32 : 64)) ? 128 : 16;
+    // 128-row tiles above 64 pairs per expert (32 for e4m3, whose products
+    // are cheap); 64-row tiles measured slower for every workload here
+    const int64_t per_expert = (int64_t)M * topk / E;
+    return per_expert > ((dtype == MOE_FP8_E4M3) ? 32 : 64) ? 128 : 16;
 }
 
 struct Carve {
