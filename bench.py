@@ -145,9 +145,45 @@ def main():
         fl = 6.0 * Mc * k * H * I
         res["layer_hbm_frac"] = lb / fused_s / (HBM_PEAK_GBS * 1e9)
         res["layer_mfma_frac"] = fl / fused_s / (MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12)
-        res["roofline_frac"] = max(lb / (HBM_PEAK_GBS * 1e9), fl / (MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12)) / fused_s
+        t_roof = max(lb / (HBM_PEAK_GBS * 1e9), fl / (MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12))
+        res["roofline_frac"] = t_roof / fused_s
         if not events:
             return res
+        # cold cache: a 512 MiB write (twice the 256 MiB Infinity Cache) before each step, outside the
+        # event pair around the step, so a small layer's weights are not served from the cache
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for i in range(min(steps, 20)):
+            flush.fill_(i & 0xff)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fused(b, ws, out, ids)
+            e1.record()
+            e1.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
+        cold.sort()
+        res["cold_ms_per_step"] = cold[len(cold) // 2]
+        res["cold_p10_p90_ms"] = [cold[len(cold) // 10], cold[(9 * len(cold)) // 10]]
+        res["cold_roofline_frac"] = t_roof / (res["cold_ms_per_step"] * 1e-3)
+        # the same step captured once in a HIP graph and replayed (launch overhead removed)
+        g = torch.cuda.CUDAGraph()
+        cap_stream = torch.cuda.Stream()
+        cap_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap_stream):
+            fused(b, ws, out, ids)  # first call on this stream outside capture
+            cap_stream.synchronize()
+            with torch.cuda.graph(g, stream=cap_stream):
+                fused(b, ws, out, ids)
+        torch.cuda.current_stream().wait_stream(cap_stream)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        res["graph_ms_per_step"] = (time.perf_counter() - t) / steps * 1e3
         # per-kernel durations through the per-step entry points, events around each launch
         # the tile height fused_moe picks for this batch
         pe = (Mc * k) // E
@@ -213,6 +249,7 @@ def main():
         if m != M:
             r = run_case(m, args.steps, args.warmup)
             sweep.append({k2: r[k2] for k2 in ("M", "ms_per_step", "tokens_per_s", "roofline_frac", "layer_hbm_frac",
+                                                "cold_ms_per_step", "cold_roofline_frac", "graph_ms_per_step",
                                                 "kernel_us", "gate_up_GBs", "down_GBs", "active_experts")})
 
     cpu = None
@@ -260,8 +297,10 @@ def main():
                    "intermediate": cfg.I, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "layer": {k2: main_res[k2] for k2 in ("roofline_frac", "layer_hbm_frac", "layer_mfma_frac", "kernel_us",
-                                              "staged_ms_per_step", "gate_up_GBs", "down_GBs", "active_experts")},
+        "layer": {k2: main_res[k2] for k2 in ("roofline_frac", "layer_hbm_frac", "layer_mfma_frac", "cold_ms_per_step",
+                                              "cold_p10_p90_ms", "cold_roofline_frac", "graph_ms_per_step",
+                                              "kernel_us", "staged_ms_per_step", "gate_up_GBs", "down_GBs",
+                                              "active_experts")},
         "sweep": sweep,
     }
     print(json.dumps(line), flush=True)

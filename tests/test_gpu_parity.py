@@ -356,3 +356,64 @@ def test_empty_batch(dev):
     out = moe.fused_moe(x, torch.empty((0, 16), device=dev), w["w1"], w["w2"], cfg.topk)
     torch.cuda.synchronize()
     assert out.shape == (0, 256)
+
+
+def test_fused_no_renormalize(dev):
+    """renormalize = 0: weights are the full softmax at the selected experts."""
+    import moe_layer_topk_amd as moe
+    cfg = replace(CONFIGS["finegrained_bf16"], E=16, H=256, I=128)
+    say("fused renormalize=0")
+    w, wh = weights(cfg, dev)
+    b = layer_batch(cfg, 24, dev)
+    out = moe.fused_moe(b["x"], b["logits"], w["w1"], w["w2"], cfg.topk, renormalize=False)
+    torch.cuda.synchronize()
+    bh = {k: (v.cpu() if v is not None else None) for k, v in b.items()}
+    ref = oracle.moe_layer("bf16", bh["x"], None, bh["logits"], wh["w1"], None, wh["w2"], None, cfg.topk,
+                           renormalize=False)
+    assert rel_err(out.cpu(), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name,M", [("finegrained_bf16", 4), ("fp8_e4m3", 8), ("mixtral_prefill_bf16", 300)])
+def test_graph_replay(dev, name, M):
+    """fused_moe captured in a HIP graph: every replay, with eager work and
+    synchronisations in between, equals the eager result bit for bit."""
+    import moe_layer_topk_amd as moe
+    cfg = CONFIGS[name]
+    if name == "fp8_e4m3":
+        cfg = replace(cfg, E=16, H=512, I=512)
+    elif name == "mixtral_prefill_bf16":
+        cfg = replace(cfg, H=1024, I=1024)  # 75 pairs per expert: the tile kernels
+    say(f"graph replay {cfg.name} M={M}")
+    w, _ = weights(cfg, dev)
+    b = layer_batch(cfg, M, dev)
+    dt = moe.moe_dtype(w["w1"])
+    ws = torch.empty(moe.fused_moe_workspace_size(dt, M, cfg.E, cfg.topk, cfg.H, cfg.I), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((M, cfg.H), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        moe.fused_moe(b["x"], b["logits"], w["w1"], w["w2"], cfg.topk, x_scale=b["x_scale"], w1_scale=w["w1_scale"],
+                      w2_scale=w["w2_scale"], workspace=ws, out=out)
+
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call()
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.zero_()
+        ws.fill_(0xA5)  # the workspace contents on entry must not matter
+        junk = torch.randn(1 << 20, device=dev).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        del junk
