@@ -149,12 +149,13 @@ def main():
         res["roofline_frac"] = t_roof / fused_s
         if not events:
             return res
-        # cold cache: a 512 MiB write (twice the 256 MiB Infinity Cache) before each step, outside the
-        # event pair around the step, so a small layer's weights are not served from the cache
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        # cold cache: a 512 MiB read (twice the 256 MiB Infinity Cache) before each step, outside the
+        # event pair around the step, so a small layer's weights are not served from the cache.  A read, not
+        # a write: dirty lines left in the cache would be written back during the step and steal bandwidth
+        flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         cold = []
         for i in range(min(steps, 20)):
-            flush.fill_(i & 0xff)
+            flush.max()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fused(b, ws, out, ids)
