@@ -136,3 +136,28 @@ def test_binding_refuses_cpu_tensors():
     import moe_layer_topk_amd as moe
     with pytest.raises(ValueError):
         moe.moe_route(torch.zeros(4, 8), 2)
+
+
+def test_quant_act_and_e4m3_down_validation(L):
+    q = L.moe_quant_act
+    assert q(FAKE, FAKE, 17, FAKE, NULL) == 2  # n not a multiple of 16
+    assert q(FAKE, FAKE, -16, FAKE, NULL) == 2
+    assert q(NULL, FAKE, 32, FAKE, NULL) == 1
+    assert q(FAKE, NULL, 32, FAKE, NULL) == 1
+    assert q(FAKE, FAKE, 32, ODD, NULL) == 5
+    assert q(NULL, NULL, 0, NULL, NULL) == 0  # n = 0: no-op
+    from moe_layer_topk_amd._lib import AlignBufs
+    bal = ctypes.byref(AlignBufs(*(0x10000,) * 6))
+    g = L.moe_grouped_gemm
+    # the e4m3-intermediate DOWN kind exists for e4m3 weights only
+    assert g(2, 1, FAKE, NULL, FAKE, NULL, bal, 4, 2, 8, 512, 256, 16, FAKE, NULL, NULL) == 3
+    assert g(2, 2, FAKE, NULL, FAKE, FAKE, bal, 4, 2, 8, 512, 256, 16, FAKE, NULL, NULL) == 1  # needs the amax
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
