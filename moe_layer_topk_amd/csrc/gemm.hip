@@ -13,11 +13,14 @@
 //             the column operand (Eq. 1), BM x 128 output tiles staged
 //             through LDS, one tile of block_m sorted rows per workgroup row.
 //
-// Both use v_mfma_f32_16x16x32_{bf16,fp8_fp8}.  Within one instruction the
-// pairing of k indices between the two operands is the same for A and B,
-// so any permutation of K applied identically to both operands leaves the
-// dot product unchanged; the loaders use that to give each lane 64
-// contiguous bytes of a row.
+// The decode family has two kernels: bf16 and e4m3 operands stream through
+// a wavefront-private LDS ring filled by direct-to-LDS copies of whole cache
+// lines (gemm_decode_ring_kernel); f32 calls, and an e4m3 down projection
+// that quantises a bf16 intermediate on load, use the register-operand
+// kernel (gemm_decode_kernel).  Within one MFMA the pairing of k indices
+// between the two operands is the same for A and B, so any permutation of K
+// applied identically to both operands leaves the dot product unchanged; the
+// loaders use that to give each lane contiguous bytes of a row.
 #include <stdlib.h>
 #include <string.h>
 
@@ -904,6 +907,278 @@ static hipError_t launch_prefill2(const GemmArgs& a, int64_t cap, hipStream_t s)
     return hipGetLastError();
 }
 
+// ------------------------------------------------------ decode (LDS ring)
+//
+// The decode work split above (blockIdx.y = active-expert slot, blockIdx.x =
+// G groups of 64 weight rows, blockIdx.z = K split; the four wavefronts take
+// K steps round robin and reduce through LDS at the end), with every operand
+// brought to the MFMAs through a wavefront-private ring of KD LDS stages
+// filled by direct-to-LDS copies.  One copy instruction moves 128 contiguous
+// bytes (a whole cache line) of each of 8 rows, where a register load in the
+// MFMA lane layout can only read 64 bytes of each of 16 rows; on MI355X the
+// whole-line pattern streams the weights about 14% faster.  A stage holds
+// 128 bytes of the group's 64 weight rows and of the pass's 16*NT token
+// rows.  No other wavefront touches a ring, so the main loop has no
+// barrier: each wave waits on its own copies with vmcnt.
+
+constexpr int kRingSB = 128;  // bytes of every row per step
+
+template <int NT, int G, int KD>
+struct DecRing {
+    static constexpr int WInstr = 64 * kRingSB / 1024;       // copy instructions for the weight rows
+    static constexpr int TInstr = NT * 16 * kRingSB / 1024;  // ... and for the token rows
+    static constexpr int Instr = WInstr + TInstr;
+    static constexpr int TokOff = 64 * kRingSB;              // token rows follow the weight rows
+    static constexpr int Stage = (64 + 16 * NT) * kRingSB;
+    static constexpr int Ring = 4 * KD * Stage;
+    static constexpr int Red = 4 * G * 4 * NT * 64 * 16;     // [4 waves][G*4 tiles][NT][64 lanes] f32x4
+    static constexpr int Lds = Ring > Red ? Ring : Red;
+    static_assert(Lds <= 160 * 1024, "LDS");
+    static_assert((KD - 1) * Instr < 64, "vmcnt range");
+};
+
+// Physical 16-byte chunk of logical chunk c in ring row r.  Rows are 128
+// bytes, so rows 2q and 2q+1 share a 256-byte bank window; XOR with q mod 8
+// puts 16 consecutive rows read at one logical chunk into 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int ring_swz(int c, int r) { return c ^ ((r >> 1) & 7); }
+
+// vmcnt wait that is also a compiler memory barrier (LDS reads of the
+// stage may not move above it)
+template <int N>
+__device__ __forceinline__ void ring_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int KIND, int DT, int NT, int G, int KD>
+__global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs g) {
+    using R = DecRing<NT, G, KD>;
+    constexpr int kElem = Opnd<DT>::kElemBytes;
+    constexpr int T = 4;  // 16-row tiles per group
+    extern __shared__ __attribute__((aligned(1024))) char ring_lds[];
+
+    const int slot = blockIdx.y;
+    if (slot >= *g.num_active) return;
+    const int e = g.active[slot];
+    const int cnt = g.counts[e];
+    const int base = g.offsets[e];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int drow = lane >> 3, dpc = lane & 7;  // copy lane: row drow of 8, physical chunk dpc
+    const int K = g.K, N = g.N, I = N / 2;
+    const size_t rowb = (size_t)K * kElem;
+    const int nks_all = (int)(rowb / kRingSB);
+    const int ks0 = (int)((long)blockIdx.z * nks_all / g.ksplit);
+    const int nks = (int)((long)(blockIdx.z + 1) * nks_all / g.ksplit) - ks0;
+    const int total = G * nks;
+    const int nw = total > wave ? (total - wave + 3) / 4 : 0;  // this wave's steps: s = wave + 4j
+
+    const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 32 * G : blockIdx.x * 64 * G;
+    const size_t gstride = (size_t)((KIND == MOE_GEMM_GATE_UP_SILU) ? 32 : 64) * rowb;
+    // source offsets of this lane's weight copies: instruction i fills group
+    // rows 8i..8i+7 (gate rows then up rows for GATE_UP)
+    const char* wexp = reinterpret_cast<const char*>(g.w) + (size_t)e * N * rowb;
+    size_t woff[R::WInstr];
+#pragma unroll
+    for (int i = 0; i < R::WInstr; ++i) {
+        const int ri = 8 * i + drow;
+        int row;
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
+            row = (ri < 32) ? n0 + ri : I + n0 + ri - 32;
+        else
+            row = n0 + ri;
+        woff[i] = (size_t)row * rowb + ring_swz(dpc, ri) * 16;
+    }
+
+    float scale = 1.0f;
+    if constexpr (DT == MOE_FP8_E4M3) {
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
+            scale = g.a_scale[0] * g.w_scale[e];
+        else
+            scale = act_scale_from_amax(g.a_scale) * g.w_scale[e];
+    }
+
+    char* ring = ring_lds + wave * (KD * R::Stage);
+    f32x4* red = reinterpret_cast<f32x4*>(ring_lds);  // after the main loop only
+    float amax = 0.0f;
+
+    for (int pass = 0; pass < cnt; pass += NT * 16) {
+        const int ntiles = min(NT, (cnt - pass + 15) / 16);
+        // token-row sources of this lane's copies (rows past the expert's
+        // count repeat its last row; their products are not used)
+        size_t toff[NT][2];
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rr = 16 * c + 8 * h + drow;
+                const int r = min(pass + rr, cnt - 1);
+                const int p = g.sorted[base + r];
+                const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
+                toff[c][h] = (size_t)src * rowb + ring_swz(dpc, rr) * 16;
+            }
+
+        auto issue = [&](int j) {
+            const int s = wave + 4 * j;
+            const int gi = s / nks, ks = ks0 + s % nks;
+            char* st = ring + (j % KD) * R::Stage;
+            // this wave's earlier LDS reads of the slot have completed
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const char* wsrc = wexp + gi * gstride + (size_t)ks * kRingSB;
+#pragma unroll
+            for (int i = 0; i < R::WInstr; ++i) lds_dma16(wsrc + woff[i], st + i * 1024);
+            const char* tsrc = reinterpret_cast<const char*>(g.a) + (size_t)ks * kRingSB;
+#pragma unroll
+            for (int c = 0; c < NT; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) lds_dma16(tsrc + toff[c][h], st + R::TokOff + (2 * c + h) * 1024);
+        };
+
+        f32x4 acc[G][T][NT];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int c = 0; c < NT; ++c) acc[gi][t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+        for (int j = 0; j < KD - 1; ++j)
+            if (j < nw) issue(j);
+        for (int j = 0; j < nw; ++j) {
+            if (j + KD - 1 < nw) {
+                issue(j + KD - 1);
+                ring_wait_vm<(KD - 1) * R::Instr>();
+            } else {
+                ring_wait_vm<0>();
+            }
+            const char* st = ring + (j % KD) * R::Stage;
+            const int gi = (wave + 4 * j) / nks;
+            const int sw = (lr >> 1) & 7;  // ring_swz of rows 16t + lr
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg) {
+                if (gg != gi) continue;
+                if constexpr (DT == MOE_FP8_E4M3) {
+                    // one f8f6f4 MFMA per tile pair covers the 128-byte step;
+                    // a lane group supplies logical chunks lg and lg + 4
+                    uint4 a0[T], a1[T];
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        const char* rp = st + (16 * t + lr) * kRingSB;
+                        a0[t] = *reinterpret_cast<const uint4*>(rp + ((lg ^ sw) << 4));
+                        a1[t] = *reinterpret_cast<const uint4*>(rp + (((lg + 4) ^ sw) << 4));
+                    }
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) {
+                        if (c < ntiles) {
+                            const char* bp = st + R::TokOff + (16 * c + lr) * kRingSB;
+                            const uint4 b0 = *reinterpret_cast<const uint4*>(bp + ((lg ^ sw) << 4));
+                            const uint4 b1 = *reinterpret_cast<const uint4*>(bp + (((lg + 4) ^ sw) << 4));
+#pragma unroll
+                            for (int t = 0; t < T; ++t) acc[gg][t][c] = mfma_f8_16x16x128(a0[t], a1[t], b0, b1, acc[gg][t][c]);
+                        }
+                    }
+                } else {
+                    // bf16: two 32-wide K chunks per step, logical chunk 4u + lg
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int pc = ((4 * u + lg) ^ sw) << 4;
+                        uint4 a[T];
+#pragma unroll
+                        for (int t = 0; t < T; ++t)
+                            a[t] = *reinterpret_cast<const uint4*>(st + (16 * t + lr) * kRingSB + pc);
+#pragma unroll
+                        for (int c = 0; c < NT; ++c) {
+                            if (c < ntiles) {
+                                const uint4 b = *reinterpret_cast<const uint4*>(st + R::TokOff + (16 * c + lr) * kRingSB + pc);
+#pragma unroll
+                                for (int t = 0; t < T; ++t) acc[gg][t][c] = Opnd<MOE_BF16>::mfma(a[t], b, acc[gg][t][c]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+
+        // every wave is done with its ring: the reduction area aliases it
+        __syncthreads();
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int c = 0; c < NT; ++c) red[((wave * G * T + gi * T + t) * NT + c) * 64 + lane] = acc[gi][t][c];
+        __syncthreads();
+
+        constexpr int kPer = (KIND == MOE_GEMM_GATE_UP_SILU) ? 2 : 4;  // output tiles per group
+        const int units = G * kPer * ntiles;
+        for (int u = wave; u < units; u += 4) {
+            const int c = u / (G * kPer);
+            const int gq = u % (G * kPer);
+            const int gi = gq / kPer, q = gq % kPer;
+            const int r = pass + c * 16 + lr;
+            if (r >= cnt) continue;
+            const int p = g.sorted[base + r];
+            if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+                f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    gs += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
+                    us += red[((w * G * T + gi * T + q + 2) * NT + c) * 64 + lane];
+                }
+                float o[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[v] = silu(gs[v] * scale) * (us[v] * scale);
+                uint2 pk;
+                pk.x = pack_bf2(o[0], o[1]);
+                pk.y = pack_bf2(o[2], o[3]);
+                if constexpr (DT == MOE_FP8_E4M3) {
+                    amax = fmaxf(amax, fabsf(bf2f(pk.x & 0xffff)));
+                    amax = fmaxf(amax, fabsf(bf2f(pk.x >> 16)));
+                    amax = fmaxf(amax, fabsf(bf2f(pk.y & 0xffff)));
+                    amax = fmaxf(amax, fabsf(bf2f(pk.y >> 16)));
+                }
+                const int n = n0 + gi * 32 + 16 * q + 4 * lg;
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * I + n) = pk;
+            } else {
+                f32x4 ys = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) ys += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
+                const int n = n0 + gi * 64 + 16 * q + 4 * lg;
+                if (g.cpart) {
+                    *reinterpret_cast<f32x4*>(g.cpart + ((size_t)blockIdx.z * g.P + p) * N + n) = ys * scale;
+                } else {
+                    uint2 pk;
+                    pk.x = pack_bf2(ys[0] * scale, ys[1] * scale);
+                    pk.y = pack_bf2(ys[2] * scale, ys[3] * scale);
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * N + n) = pk;
+                }
+            }
+        }
+        // the next pass refills the rings over the reduction area
+        __syncthreads();
+    }
+    if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) amax_publish(amax, g.c_amax);
+}
+
+template <int KIND, int DT, int NT, int G, int KD>
+static hipError_t launch_decode_ring(const GemmArgs& a, int nslots, hipStream_t s) {
+    using R = DecRing<NT, G, KD>;
+    const int rows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 * G : 64 * G;  // output columns per workgroup
+    const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
+    // LDS above the default dynamic limit must be requested once per kernel
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_ring_kernel<KIND, DT, NT, G, KD>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, R::Lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gemm_decode_ring_kernel<KIND, DT, NT, G, KD>), dim3(ncols / rows, nslots, a.ksplit),
+                       dim3(kDecThreads), R::Lds, s, a);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- f32
 //
 // Plain fp32 path: one thread per (sorted row, output column), dot products
@@ -977,12 +1252,21 @@ GemmPath choose_gemm_path(const GemmCall& g) {
 
 template <int KIND, int DT, int NT, int G, bool AQ>
 static hipError_t launch_decode_ntga(const GemmArgs& a, int nslots, hipStream_t s) {
-    const int rows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 * G : 64 * G;  // output columns per workgroup
-    const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
-    const size_t lds = sizeof(f32x4) * 4 * G * 4 * NT * 64;
-    hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT, G, AQ>), dim3(ncols / rows, nslots, a.ksplit),
-                       dim3(kDecThreads), lds, s, a);
-    return hipGetLastError();
+    // operands whose rows the MFMAs read as stored go through the LDS ring
+    // kernel; f32 calls and a bf16 intermediate quantised on load do not
+    constexpr bool kRing = DT != MOE_F32 && !(KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3 && !AQ);
+    // (two stages per ring: measured as fast as three on every decode
+    // workload, and it leaves LDS for a second workgroup at one token tile)
+    if constexpr (kRing) {
+        return launch_decode_ring<KIND, DT, NT, G, 2>(a, nslots, s);
+    } else {
+        const int rows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 * G : 64 * G;  // output columns per workgroup
+        const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
+        const size_t lds = sizeof(f32x4) * 4 * G * 4 * NT * 64;
+        hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT, G, AQ>), dim3(ncols / rows, nslots, a.ksplit),
+                           dim3(kDecThreads), lds, s, a);
+        return hipGetLastError();
+    }
 }
 
 template <int KIND, int DT, int NT, int G>
@@ -1008,8 +1292,10 @@ static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_es
         // each workgroup little to stream against its fixed costs: four row
         // groups (128-expert layer, K = 768: 2-3% faster at 16 and 256 tokens)
         const long steps = (long)a.K * Opnd<DT>::kElemBytes / kDecSpan;
-        if (NT < 4 && steps <= 8 && a.ksplit == 1 && ncols % 256 == 0 && (long)(ncols / 256) * active_est >= 256)
-            return launch_decode_ntg<KIND, DT, NT, 4>(a, nslots, s);
+        if constexpr (NT < 4) {
+            if (steps <= 8 && a.ksplit == 1 && ncols % 256 == 0 && (long)(ncols / 256) * active_est >= 256)
+                return launch_decode_ntg<KIND, DT, NT, 4>(a, nslots, s);
+        }
     }
     if (two && a.ksplit == 1 && ncols % rows2 == 0) return launch_decode_ntg<KIND, DT, NT, 2>(a, nslots, s);
     return launch_decode_ntg<KIND, DT, NT, 1>(a, nslots, s);
