@@ -294,6 +294,138 @@ __device__ __forceinline__ void align_core(GetId get_id, int P, int E, int block
     }
 }
 
+// ----------------------------------------------------- align, one workgroup
+//
+// Up to 1024 pairs (thread p owns pair p): the same outputs as align_core
+// in four barriers and no LDS atomics.
+//  1. ids to LDS (or routed here: wavefront w routes token w).
+//  2. Within a wavefront, lanes holding the same expert are found with eight
+//     ballots and ranked by popcount; the lowest lane records the count in
+//     wcnt[wave][e].
+//  3. Wavefront 0 totals each expert over the wavefronts, scans the padded
+//     counts and writes counts, offsets and the active-expert list.
+//  4. Pair p goes to offsets[e] + (pairs of e in earlier wavefronts) + rank.
+//     Each tile's expert is found once (binary search over the offsets);
+//     every row that is not a real row of its tile's expert gets sentinel P.
+
+constexpr int kSmallMaxPairs = kAlignThreads;
+constexpr int kSmallMaxTiles = kAlignThreads;  // cap/block_m <= min(E,P) + P/block_m <= 1024 (see moe_align_capacity)
+
+template <bool ROUTE>
+__global__ void __launch_bounds__(kAlignThreads) align_small_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ ids_in, int M, int E, int topk, int renormalize,
+    int32_t* __restrict__ ids_out, float* __restrict__ weights_out, int block_m, int cap,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ active, int32_t* __restrict__ num_active,
+    float* __restrict__ zero_f32) {
+    __shared__ int ids_s[kSmallMaxPairs];
+    __shared__ int wcnt[kAlignWaves][kMaxE];
+    __shared__ int off_s[kMaxE + 1];
+    __shared__ int cnt_s[kMaxE];
+    __shared__ int tile_s[kSmallMaxTiles];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int P = M * topk;
+    if (tid == 0 && zero_f32) *zero_f32 = 0.0f;
+    for (int i = tid; i < kAlignWaves * kMaxE; i += kAlignThreads) (&wcnt[0][0])[i] = 0;
+    if constexpr (ROUTE) {
+        if (wave < M) {
+            int sel;
+            float w;
+            route_token(logits + (size_t)wave * E, E, topk, renormalize, &sel, &w);
+            if (lane < topk) {
+                ids_out[(size_t)wave * topk + lane] = sel;
+                weights_out[(size_t)wave * topk + lane] = w;
+                ids_s[wave * topk + lane] = sel;
+            }
+        }
+    } else {
+        if (tid < P) ids_s[tid] = ids_in[tid];
+    }
+    __syncthreads();
+
+    const int e = (tid < P) ? ids_s[tid] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const uint64_t bb = __ballot(valid && ((e >> b) & 1));
+        same &= ((e >> b) & 1) ? bb : ~bb;
+    }
+    const int rank = __popcll(same & lanemask_lt());
+    if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
+    __syncthreads();
+
+    if (wave == 0) {
+        // lane handles experts 4*lane .. 4*lane+3
+        int c[4], pc[4], act[4];
+        int s = 0, a = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ex = 4 * lane + q;
+            c[q] = 0;
+            if (ex < E)
+#pragma unroll
+                for (int w = 0; w < kAlignWaves; ++w) c[q] += wcnt[w][ex];
+            pc[q] = (c[q] + block_m - 1) / block_m * block_m;
+            act[q] = c[q] > 0;
+            s += pc[q];
+            a += act[q];
+        }
+        const int incl = wave_incl_scan(s);
+        const int aincl = wave_incl_scan(a);
+        int run = incl - s, arun = aincl - a;
+        const int nact_total = __shfl(aincl, 63, 64);
+        const int amax = P < E ? P : E;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ex = 4 * lane + q;
+            if (ex < E) {
+                off_s[ex] = run;
+                cnt_s[ex] = c[q];
+                offsets_out[ex] = run;
+                counts_out[ex] = c[q];
+                if (act[q]) active[arun] = ex;
+            }
+            run += pc[q];
+            arun += act[q];
+        }
+        if (lane == 63) {
+            off_s[E] = run;
+            offsets_out[E] = run;
+            *num_active = nact_total;
+        }
+        for (int i = nact_total + lane; i < amax; i += 64) active[i] = -1;
+    }
+    __syncthreads();
+
+    if (valid) {
+        int pos = off_s[e] + rank;
+        for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+        sorted[pos] = tid;
+    }
+    const int total = off_s[E];
+    const int ntiles = cap / block_m;
+    for (int t = tid; t < ntiles; t += kAlignThreads) {
+        const int r = t * block_m;
+        int ex = -1;
+        if (r < total) {
+            int lo = 0, hi = E - 1;  // last expert with off_s <= r
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off_s[mid] <= r) lo = mid; else hi = mid - 1;
+            }
+            ex = lo;
+        }
+        tile_s[t] = ex;
+        tile_expert[t] = ex;
+    }
+    __syncthreads();
+    for (int r = tid; r < cap; r += kAlignThreads) {
+        const int ex = tile_s[r / block_m];
+        if (ex < 0 || r - off_s[ex] >= cnt_s[ex]) sorted[r] = P;
+    }
+}
+
 __global__ void __launch_bounds__(kAlignThreads) align_kernel(
     const int32_t* __restrict__ ids, int P, int E, int block_m, int cap, int32_t* __restrict__ sorted,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ counts_out,
@@ -308,6 +440,12 @@ hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m,
                         const moe_align_bufs& out, float* zero_f32, hipStream_t s) {
     if (M == 0) return hipSuccess;
     const int P = M * topk;
+    if (P <= kSmallMaxPairs) {
+        hipLaunchKernelGGL((align_small_kernel<false>), dim3(1), dim3(kAlignThreads), 0, s, nullptr, ids, M, E, topk,
+                           1, nullptr, nullptr, block_m, (int)cap, out.sorted_ids, out.tile_expert,
+                           out.expert_counts, out.expert_offsets, out.active_experts, out.num_active, zero_f32);
+        return hipGetLastError();
+    }
     // every workgroup reads all P ids, so their number is capped: past 64 K
     // pairs a workgroup scatters several 1024-pair sub-chunks
     const int units = (P + kAlignThreads - 1) / kAlignThreads;
@@ -320,44 +458,21 @@ hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m,
 }
 
 // Small batches (M <= 16): one launch for both steps.  Wavefront w routes
-// token w (the same code as route_kernel), the ids go to LDS and to the
-// outputs, and after a barrier the workgroup aligns them.  Saves a launch and
-// the dependency gap between the two, which dominate at a few tokens.
+// token w (route_token, as route_kernel does), the ids go to LDS and to the
+// outputs, and after a barrier the workgroup aligns them (align_small_kernel
+// with ROUTE).  Saves a launch and the dependency gap between the two, which
+// dominate at a few tokens.
 constexpr int kRouteAlignMaxM = kAlignWaves;
-
-__global__ void __launch_bounds__(kAlignThreads) route_align_kernel(
-    const float* __restrict__ logits, int M, int E, int topk, int renormalize, int32_t* __restrict__ ids,
-    float* __restrict__ weights, int block_m, int cap, int32_t* __restrict__ sorted,
-    int32_t* __restrict__ tile_expert, int32_t* __restrict__ counts_out, int32_t* __restrict__ offsets_out,
-    int32_t* __restrict__ active, int32_t* __restrict__ num_active, float* __restrict__ zero_f32) {
-    __shared__ int ids_s[kRouteAlignMaxM * kMaxTopk];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (threadIdx.x == 0 && zero_f32) *zero_f32 = 0.0f;
-    if (wave < M) {
-        int sel;
-        float w;
-        route_token(logits + (size_t)wave * E, E, topk, renormalize, &sel, &w);
-        if (lane < topk) {
-            ids[(size_t)wave * topk + lane] = sel;
-            weights[(size_t)wave * topk + lane] = w;
-            ids_s[wave * topk + lane] = sel;
-        }
-    }
-    __syncthreads();
-    align_core([&](int p) { return ids_s[p]; }, M * topk, E, block_m, cap, 0, 1, kAlignThreads, sorted, tile_expert,
-               counts_out,
-               offsets_out, active, num_active);
-}
 
 bool route_align_fits(int M) { return M > 0 && M <= kRouteAlignMaxM; }
 
 hipError_t launch_route_align(const float* logits, int M, int E, int topk, int renormalize, int32_t* ids,
                               float* weights, int block_m, int64_t cap, const moe_align_bufs& out,
                               float* zero_f32, hipStream_t s) {
-    if (!route_align_fits(M)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_align_kernel, dim3(1), dim3(kAlignThreads), 0, s, logits, M, E, topk, renormalize, ids,
-                       weights, block_m, (int)cap, out.sorted_ids, out.tile_expert, out.expert_counts,
-                       out.expert_offsets, out.active_experts, out.num_active, zero_f32);
+    if (!route_align_fits(M) || M * topk > kSmallMaxPairs) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((align_small_kernel<true>), dim3(1), dim3(kAlignThreads), 0, s, logits, nullptr, M, E, topk,
+                       renormalize, ids, weights, block_m, (int)cap, out.sorted_ids, out.tile_expert,
+                       out.expert_counts, out.expert_offsets, out.active_experts, out.num_active, zero_f32);
     return hipGetLastError();
 }
 
