@@ -258,15 +258,19 @@ def main():
         import oracle
         b = layer_batch(cfg, M, "cpu")
         wh = {k2: (v.cpu() if v is not None else None) for k2, v in w.items()}
-        amax = None
-        t = time.perf_counter()
-        if cfg.dtype == "fp8":
-            amax = oracle.act_amax("fp8", b["x"], b["x_scale"], b["logits"], wh["w1"], wh["w1_scale"], cfg.topk)
-        oracle.moe_layer(cfg.dtype, b["x"], b["x_scale"], b["logits"], wh["w1"], wh["w1_scale"], wh["w2"],
-                         wh["w2_scale"], cfg.topk, act_amax_value=amax)
-        el = time.perf_counter() - t
-        cpu = {"value": M / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"the full {M}-token batch of the timed workload, once ({el:.2f} s)"}
+        # the whole batch, repeated until about 10 s of CPU work (at most 8 passes)
+        passes, el = 0, 0.0
+        while passes == 0 or (el < 10.0 and passes < 8):
+            amax = None
+            t = time.perf_counter()
+            if cfg.dtype == "fp8":
+                amax = oracle.act_amax("fp8", b["x"], b["x_scale"], b["logits"], wh["w1"], wh["w1_scale"], cfg.topk)
+            oracle.moe_layer(cfg.dtype, b["x"], b["x_scale"], b["logits"], wh["w1"], wh["w1_scale"], wh["w2"],
+                             wh["w2_scale"], cfg.topk, act_amax_value=amax)
+            el += time.perf_counter() - t
+            passes += 1
+        cpu = {"value": M * passes / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"the full {M}-token batch of the timed workload, {passes} pass(es) ({el:.2f} s)"}
 
     # roofline of the dominant kernel (gate/up): HBM-bound when its weight
     # bytes take longer at peak bandwidth than its flops at peak MFMA rate
