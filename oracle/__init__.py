@@ -51,6 +51,7 @@ def lib():
         i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         sig = {
             "oracle_bf16_decode": (dbl, [ctypes.c_uint16]),
+            "oracle_bf16_round": (dbl, [dbl]),
             "oracle_e4m3_decode": (dbl, [ctypes.c_uint8]),
             "oracle_e4m3_encode": (ctypes.c_uint8, [dbl]),
             "oracle_num_threads": (i32, []),
@@ -106,6 +107,11 @@ def num_threads() -> int:
 
 def bf16_decode(bits: int) -> float:
     return lib().oracle_bf16_decode(bits)
+
+
+def bf16_round(v: float) -> float:
+    """The nearest bfloat16 value of v (ties to even), as a float."""
+    return lib().oracle_bf16_round(v)
 
 
 def e4m3_decode(code: int) -> float:

@@ -319,6 +319,23 @@ def test_fused_prefill_shapes(dev, E, k, H, I, M):
     check_layer(cfg, M, dev, tokens=np.arange(0, M, 7))
 
 
+# extreme and degenerate layer shapes: the most experts and slots the ABI
+# takes, a single expert (a dense SwiGLU FFN), top-k equal to E (every expert
+# active), two experts sharing every token (prefill tiles holding both), and
+# rows shorter than one 256-byte step per wavefront
+EDGE_LAYERS = [("bf16", 256, 16, 256, 256, 33), ("bf16", 1, 1, 128, 128, 5), ("f32", 1, 1, 128, 128, 5),
+               ("bf16", 8, 8, 128, 128, 1), ("bf16", 2, 2, 256, 128, 300), ("fp8", 256, 16, 256, 256, 20),
+               ("fp8", 4, 4, 256, 256, 3)]
+
+
+@pytest.mark.parametrize("dtype,E,k,H,I,M", EDGE_LAYERS)
+def test_fused_edge_shapes(dev, dtype, E, k, H, I, M):
+    base = {"f32": "tiny_f32", "bf16": "finegrained_bf16", "fp8": "fp8_e4m3"}[dtype]
+    cfg = replace(CONFIGS[base], E=E, topk=k, H=H, I=I, router="normal")
+    say(f"fused edge {dtype} E={E} k={k} H={H} I={I} M={M}")
+    check_layer(cfg, M, dev)
+
+
 def test_fused_layer_full_prefill(dev):
     say("fused mixtral_prefill_bf16 M=4096 (sampled tokens)")
     check_layer(CONFIGS["mixtral_prefill_bf16"], 4096, dev, tokens=[0, 1, 2, 1000, 2047, 3000, 4094, 4095])
