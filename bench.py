@@ -43,15 +43,20 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources the grouped-GEMM kernels are built from: measured counter traffic of the
-    gate/up launch is only reported for the kernel code it was taken on."""
+    """Hash of the code the grouped-GEMM kernels are built from (comments and
+    whitespace removed): measured counter traffic of the gate/up launch is only
+    reported for the kernel code it was taken on."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for f in (os.path.join(ROOT, "moe_layer_topk_amd", "csrc", n) for n in ("gemm.hip", "moe_device.h", "moe_launch.h")):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    with open(os.path.join(ROOT, "include", "moe.h"), "rb") as fh:
-        h.update(fh.read())
+    files = [os.path.join(ROOT, "moe_layer_topk_amd", "csrc", n) for n in ("gemm.hip", "moe_device.h", "moe_launch.h")]
+    files.append(os.path.join(ROOT, "include", "moe.h"))
+    for f in files:
+        with open(f) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -939,10 +939,12 @@ static hipError_t launch_prefill2(const GemmArgs& a, int64_t cap, int E, hipStre
 // filled by direct-to-LDS copies.  One copy instruction moves 128 contiguous
 // bytes (a whole cache line) of each of 8 rows, where a register load in the
 // MFMA lane layout can only read 64 bytes of each of 16 rows; on MI355X the
-// whole-line pattern streams the weights about 14% faster.  A stage holds
-// 128 bytes of the group's 64 weight rows and of the pass's 16*NT token
-// rows.  No other wavefront touches a ring, so the main loop has no
-// barrier: each wave waits on its own copies with vmcnt.
+// whole-line pattern streams the weights about 14% faster, and the weight
+// copies carry the non-temporal hint (read once; another 13%), the token
+// copies not (they are re-read by every row group).  A stage holds 128
+// bytes of the group's 64 weight rows and of the pass's 16*NT token rows.
+// No other wavefront touches a ring, so the main loop has no barrier: each
+// wave waits on its own copies with vmcnt.
 
 constexpr int kRingSB = 128;  // bytes of every row per step
 
