@@ -28,11 +28,15 @@ _DT = {"f32": OR_F32, "bf16": OR_BF16, "fp8": OR_FP8}
 
 
 def build(force: bool = False) -> str:
-    """Compile moe_oracle.c with gcc (-O2, OpenMP; no -ffast-math)."""
+    """Compile moe_oracle.c with gcc: -O3, OpenMP, no -ffast-math and no FMA
+    contraction (every product and sum rounds as written).  The target is
+    x86-64-v3 (AVX2/FMA) rather than -march=native: the library is built once
+    and also runs on other hosts, whose CPU may lack what this one has."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(
-            ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math", "-std=c11",
+            ["gcc", "-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp",
+             "-fno-fast-math", "-std=c11",
              "-Wall", "-Wextra", "-Wno-unused-parameter", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -51,7 +55,6 @@ def lib():
         i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         sig = {
             "oracle_bf16_decode": (dbl, [ctypes.c_uint16]),
-            "oracle_bf16_round": (dbl, [dbl]),
             "oracle_e4m3_decode": (dbl, [ctypes.c_uint8]),
             "oracle_e4m3_encode": (ctypes.c_uint8, [dbl]),
             "oracle_num_threads": (i32, []),
@@ -107,11 +110,6 @@ def num_threads() -> int:
 
 def bf16_decode(bits: int) -> float:
     return lib().oracle_bf16_decode(bits)
-
-
-def bf16_round(v: float) -> float:
-    """The nearest bfloat16 value of v (ties to even), as a float."""
-    return lib().oracle_bf16_round(v)
 
 
 def e4m3_decode(code: int) -> float:

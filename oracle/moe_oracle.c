@@ -27,11 +27,11 @@
  *  - FP8 (MoE kernel engineering post, "FP8 backend routing" section: one
  *    scale per tensor): x and the weights are e4m3 codes times their float32
  *    scale; the intermediate a is quantised with one dynamic per-tensor
- *    scale, then dequantised before the down projection.  The pages leave the
- *    intermediate's precision open; it is held as bfloat16 (the kernel's
- *    storage), so the quantisation decision is taken on bf16(a): s =
- *    amax/448 with amax the largest |bf16(a)| over every pair (float32
- *    division, as the kernel does), code = e4m3(bf16(a) / s).
+ *    scale, then dequantised before the down projection: s = amax/448 with
+ *    amax the largest |a| of this float64 intermediate over every pair, and
+ *    code = e4m3(f32(a) / s) with a float32 division.  The pages leave the
+ *    intermediate's precision open; the oracle keeps its own float64 value
+ *    up to that one decision.
  *
  * Codecs are written from the formats' definitions: bfloat16 is the upper
  * half of an IEEE binary32; OCP OFP8 E4M3 has 1 sign, 4 exponent (bias 7)
@@ -97,27 +97,6 @@ uint8_t oracle_e4m3_encode(double v) {
     int ef = e + 7;
     if (ef > 15 || (ef == 15 && n - 8.0 > 6.0)) return sign | 0x7E;
     return sign | (uint8_t)(ef << 3) | (uint8_t)(n - 8.0);
-}
-
-/* bf16(v): round a float64 to the nearest bfloat16 value (8 significant
- * bits, ties to even), returned as a float64; normal range quantum
- * 2^(e-7) for v in [2^e, 2^(e+1)), subnormal quantum 2^-133. */
-double oracle_bf16_round(double v) {
-    if (isnan(v) || isinf(v) || v == 0.0) return v;
-    double a = fabs(v);
-    int ex;
-    frexp(a, &ex);
-    int e = ex - 1;
-    if (e < -126) e = -126;
-    double q = ldexp(1.0, e - 7);
-    double r = a / q; /* exact: q is a power of two */
-    double fl = floor(r);
-    double fr = r - fl;
-    double n = fl;
-    if (fr > 0.5 || (fr == 0.5 && fmod(fl, 2.0) != 0.0)) n = fl + 1.0;
-    double out = n * q; /* a carry into the next binade is exact */
-    if (out >= ldexp(1.0, 128)) out = INFINITY;
-    return signbit(v) ? -out : out;
 }
 
 static double elem(int dtype, const void* base, int64_t i) {
@@ -250,20 +229,19 @@ void oracle_down(int dtype, const double* a, const void* w2_e, double w2_scale, 
 }
 
 /* The fp8 intermediate: s = f32(amax)/448 in float32 (1 if amax is 0),
- * code = e4m3(bf16(a)/s) with float32 division (bf16 values are exact in
- * float32), value = decode(code)*s. */
+ * code = e4m3(f32(a)/s) with float32 division, value = decode(code)*s. */
 void oracle_quant_act(double* a, int64_t I, double amax) {
     float s = (float)amax / 448.0f;
     if (!(amax > 0.0)) s = 1.0f;
     for (int64_t i = 0; i < I; ++i) {
-        float v = (float)oracle_bf16_round(a[i]) / s;
+        float v = (float)a[i] / s;
         a[i] = oracle_e4m3_decode(oracle_e4m3_encode((double)v)) * (double)s;
     }
 }
 
 static double sc(const float* p, int64_t i) { return p ? (double)p[i] : 1.0; }
 
-/* Largest |bf16(a)| over every (token, slot) pair of the batch: the dynamic
+/* Largest |a| over every (token, slot) pair of the batch: the dynamic
  * per-tensor statistic of the fp8 intermediate. */
 int oracle_act_amax(int dtype, const void* x, const float* x_scale, const float* logits, const void* w1,
                     const float* w1_scale, int64_t M, int E, int k, int64_t H, int64_t I, int renorm,
@@ -291,10 +269,8 @@ int oracle_act_amax(int dtype, const void* x, const float* x_scale, const float*
                 int e = ids[j];
                 oracle_gate_up(dtype, (const char*)x + (size_t)t * H * eb, sc(x_scale, 0),
                                (const char*)w1 + (size_t)e * 2 * I * H * eb, sc(w1_scale, e), H, I, a);
-                for (int64_t n = 0; n < I; ++n) {
-                    const double m = fabs(oracle_bf16_round(a[n]));
-                    if (m > local) local = m;
-                }
+                for (int64_t n = 0; n < I; ++n)
+                    if (fabs(a[n]) > local) local = fabs(a[n]);
             }
         }
 #pragma omp critical
@@ -307,7 +283,7 @@ int oracle_act_amax(int dtype, const void* x, const float* x_scale, const float*
     return err;
 }
 
-/* Per-token version of oracle_act_amax: amax_out[t] = largest |bf16(a)| over the
+/* Per-token version of oracle_act_amax: amax_out[t] = largest |a| over the
  * token's k pairs, so the batch statistic of any prefix of tokens is the max
  * of a prefix of this array. */
 int oracle_act_amax_per_token(int dtype, const void* x, const float* x_scale, const float* logits,
@@ -335,10 +311,8 @@ int oracle_act_amax_per_token(int dtype, const void* x, const float* x_scale, co
                 int e = ids[j];
                 oracle_gate_up(dtype, (const char*)x + (size_t)t * H * eb, sc(x_scale, 0),
                                (const char*)w1 + (size_t)e * 2 * I * H * eb, sc(w1_scale, e), H, I, a);
-                for (int64_t n = 0; n < I; ++n) {
-                    const double m = fabs(oracle_bf16_round(a[n]));
-                    if (m > local) local = m;
-                }
+                for (int64_t n = 0; n < I; ++n)
+                    if (fabs(a[n]) > local) local = fabs(a[n]);
             }
             amax_out[t] = local;
         }

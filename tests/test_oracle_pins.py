@@ -9,7 +9,6 @@
 - E=1, k=1: the dense SwiGLU FFN through torch CPU matmuls
 - token order: permutation invariance
 - e4m3 codec: torch's float8_e4m3fn (exhaustive decode; encode after clamping)
-- bf16 rounding of the fp8 intermediate: torch's float32 -> bfloat16 cast
 - fp8 scaling: scale-product invariance and a brute force that quantises the
   intermediate with torch's cast
 """
@@ -327,31 +326,6 @@ def test_fp8_scale_product_invariance_bitwise():
     assert np.array_equal(out3, out * 4)
 
 
-def _bf16_nearest(a):
-    """Nearest bfloat16 values (8 significant bits, ties to even) of float64s,
-    from frexp and numpy's half-to-even rounding."""
-    a = np.asarray(a, np.float64)
-    m, e = np.frexp(np.abs(a))                 # |a| = m * 2^e, m in [0.5, 1)
-    q = np.ldexp(1.0, np.maximum(e, -125) - 8)  # quantum: 2^-7 of the binade's lower bound
-    return np.sign(a) * np.round(np.abs(a) / q) * q
-
-
-def test_bf16_round_vs_torch_cast():
-    """oracle.bf16_round on float32 inputs (random, exact ties, subnormals,
-    binade edges) against torch's float32 -> bfloat16 cast."""
-    rng = np.random.default_rng(31)
-    v = (rng.standard_normal(4000) * np.exp2(rng.integers(-40, 40, 4000))).astype(np.float32)
-    ties = (np.arange(1, 200, dtype=np.float32) * 2 + 1) * np.float32(2.0 ** -8)  # odd multiples of half a quantum
-    edge = np.array([1.0, -1.0, 2.0 - 2.0 ** -9, 255.96875, 1e-40, -3e-39, 0.0], np.float32)
-    vals = np.concatenate([v, ties.astype(np.float32), edge])
-    ref = torch.from_numpy(vals).to(torch.bfloat16).double().numpy()
-    got = np.array([oracle.bf16_round(float(t)) for t in vals])
-    assert np.array_equal(got, ref)
-    # float64 inputs are rounded once, from the exact value (not through float32)
-    just_above_tie = 1.0 + 2.0 ** -8 + 2.0 ** -40
-    assert oracle.bf16_round(just_above_tie) == 1.0 + 2.0 ** -7
-
-
 def test_fp8_layer_matches_brute_force_with_torch_codec():
     xq, sx, lg, w1, s1, w2, s2, k = _fp8_case(22)
     x = xq.double().numpy() * float(sx)
@@ -359,18 +333,18 @@ def test_fp8_layer_matches_brute_force_with_torch_codec():
     w2d = w2.double().numpy() * s2.double().numpy()[:, None, None]
     E, twoI, H = w1d.shape
     I = twoI // 2
-    # the intermediate is held as bfloat16: amax over every pair's bf16(a)
+    # amax over every pair's float64 intermediate
     ids, _ = np_route(lg, k)
     amax = 0.0
     for t in range(x.shape[0]):
         for j in range(k):
             h = w1d[ids[t, j]] @ x[t]
-            amax = max(amax, np.abs(_bf16_nearest(silu(h[:I]) * h[I:])).max())
-    assert oracle.act_amax("fp8", xq, sx, lg, w1, s1, k) == amax
+            amax = max(amax, np.abs(silu(h[:I]) * h[I:]).max())
+    assert abs(oracle.act_amax("fp8", xq, sx, lg, w1, s1, k) - amax) <= 1e-12 * amax
     s = np.float32(amax) / np.float32(448.0)
 
     def q(a):
-        v = torch.from_numpy((_bf16_nearest(a).astype(np.float32) / s).astype(np.float32)).clamp(-448, 448)
+        v = torch.from_numpy((a.astype(np.float32) / s).astype(np.float32)).clamp(-448, 448)
         return v.to(torch.float8_e4m3fn).double().numpy() * float(s)
 
     ref = dense_masked(x, w1d, w2d, lg, k, act_fn=q)
