@@ -114,15 +114,17 @@ moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t E
  *  dtype: MOE_F32 (a, w, c float32), MOE_BF16 (a, w, c bfloat16),
  *         MOE_FP8_E4M3 (w e4m3 with w_scale[E] float32 per expert matrix;
  *         GATE_UP: a = x e4m3 with a_scale -> its float32 scale, c = act
- *         bfloat16, c_amax -> float32 that receives max|act| (zeroed by the
- *         call itself); DOWN: a = act bfloat16, a_scale -> that amax, the act
- *         rows are quantised on load with s = amax/448, c = y bfloat16).
+ *         float32 (the intermediate stays in float32 until it is quantised),
+ *         c_amax -> float32 that receives max|act| (zeroed by the call
+ *         itself); DOWN: a = act float32, a_scale -> that amax, the act rows
+ *         are quantised on load with one per-tensor scale s = amax/448: code
+ *         = e4m3(act / s), IEEE float32 quotient, round to nearest even,
+ *         saturating at +-448; c = y bfloat16).
  *  kind = MOE_GEMM_DOWN_E4M3_ACT (MOE_FP8_E4M3 only): as MOE_GEMM_DOWN, but a
  *         holds the e4m3 codes [P][K] that moe_quant_act wrote for the same
- *         amax, and a_scale -> that amax.  The products are those of
- *         MOE_GEMM_DOWN (same codes, same scales); the act rows are read at
- *         one byte per element, and a kernel that needs the codes in LDS
- *         serves the call, so results agree with MOE_GEMM_DOWN to rounding.
+ *         amax, and a_scale -> that amax.  Same codes, same scales, same
+ *         products as MOE_GEMM_DOWN; the rows are read at one byte per value
+ *         (what the tile kernels want when many rows share an expert).
  *  a_scale, w_scale, c_amax must be NULL unless dtype is MOE_FP8_E4M3.
  *  al, block_m: the output of moe_align for the same topk_ids and block_m.
  *  Rows of a expert's run are read through al->sorted_ids; only the first
@@ -134,11 +136,12 @@ moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, 
                             int32_t topk, int32_t E, int32_t N, int32_t K, int32_t block_m, void* c,
                             float* c_amax, void* stream);
 
-/* Per-tensor e4m3 quantisation of the bfloat16 intermediate, the scaling the
- * fp8 down projection needs (MoE kernel engineering post, the FP8 part of
- * its kernel section): s = amax / 448 in float32, code = e4m3 of act / s with
- * an IEEE float32 division, round to nearest even, saturating at +-448.
- *  act    device bfloat16 [n]
+/* Per-tensor e4m3 quantisation of the float32 intermediate, the scaling the
+ * fp8 down projection needs (MoE kernel engineering post, FP8 backend-routing
+ * section: one scale per tensor): s = amax / 448 in float32, code = e4m3 of
+ * act / s with an IEEE float32 quotient, round to nearest even, saturating
+ * at +-448 (the codes the e4m3 DOWN call forms on load).
+ *  act    device float32 [n]
  *  amax   device float32 [1], > 0 (as written by the fp8 GATE_UP GEMM)
  *  act_q  device uint8 [n], e4m3 codes
  * n must be a multiple of 16 (MOE_ERR_SHAPE otherwise); n = 0 is a no-op. */

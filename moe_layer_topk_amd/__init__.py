@@ -7,8 +7,9 @@ kernels; there is no CPU or framework fallback (a missing library raises).
 
 Steps of the layer (FusedMoE vs MegaMoE post, sections 2 and 3.1):
 moe_route -> moe_align -> moe_grouped_gemm (gate/up + SiLU-and-mul, then
-down; for e4m3 weights moe_quant_act between the two) -> moe_combine, or all
-of them in one call with fused_moe.
+down) -> moe_combine, or all of them in one call with fused_moe.  For e4m3
+weights the intermediate is float32 and the down call quantises it on load;
+moe_quant_act gives the same codes as a tensor.
 """
 from __future__ import annotations
 
@@ -30,7 +31,8 @@ from ._lib import (  # noqa: F401
 )
 
 _DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3}
-_INTER = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.bfloat16}
+_INTER = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.bfloat16}  # y and out
+_ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.float32}  # the intermediate
 
 
 def _p(t):
@@ -98,9 +100,11 @@ def moe_grouped_gemm(kind: int, a: torch.Tensor, w: torch.Tensor, al: dict, M: i
     P = M * topk
     cols = N // 2 if kind == MOE_GEMM_GATE_UP_SILU else N
     if kind != MOE_GEMM_GATE_UP_SILU and (kind == MOE_GEMM_DOWN_E4M3_ACT) != (a.dtype == torch.float8_e4m3fn):
-        raise ValueError("MOE_GEMM_DOWN_E4M3_ACT takes e4m3 act codes and e4m3 weights; DOWN takes the bf16 act")
+        raise ValueError("MOE_GEMM_DOWN_E4M3_ACT takes e4m3 act codes and e4m3 weights; DOWN takes the act")
+    if kind != MOE_GEMM_GATE_UP_SILU and kind != MOE_GEMM_DOWN_E4M3_ACT and a.dtype != _ACT[dt]:
+        raise ValueError(f"DOWN with {w.dtype} weights takes a {_ACT[dt]} intermediate, got {a.dtype}")
     if c is None:
-        c = torch.empty((P, cols), dtype=_INTER[dt], device=w.device)
+        c = torch.empty((P, cols), dtype=_ACT[dt] if kind == MOE_GEMM_GATE_UP_SILU else _INTER[dt], device=w.device)
     if dt == MOE_FP8_E4M3 and kind == MOE_GEMM_GATE_UP_SILU and c_amax is None:
         c_amax = torch.empty(1, dtype=torch.float32, device=w.device)
     bufs = align_struct(al)
@@ -110,9 +114,9 @@ def moe_grouped_gemm(kind: int, a: torch.Tensor, w: torch.Tensor, al: dict, M: i
 
 
 def moe_quant_act(act: torch.Tensor, amax: torch.Tensor, out=None):
-    """e4m3 codes (torch.float8_e4m3fn, same shape) of the bfloat16 intermediate with scale amax/448."""
-    if act.dtype != torch.bfloat16:
-        raise ValueError("moe_quant_act takes the bfloat16 intermediate")
+    """e4m3 codes (torch.float8_e4m3fn, same shape) of the float32 intermediate with scale amax/448."""
+    if act.dtype != torch.float32:
+        raise ValueError("moe_quant_act takes the float32 intermediate")
     q = out if out is not None else torch.empty(act.shape, dtype=torch.float8_e4m3fn, device=act.device)
     check(lib().moe_quant_act(_p(act), _p(amax), act.numel(), _p(q), _stream(act)), "moe_quant_act")
     return q

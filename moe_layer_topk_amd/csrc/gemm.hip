@@ -75,20 +75,47 @@ __device__ __forceinline__ f32x4 mfma_f8_16x16x128(const uint4& a0, const uint4&
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// 8 bf16 activations quantised to 8 e4m3 codes with value/s (IEEE division).
-__device__ __forceinline__ uint2 quant8(const uint4& v, float s) {
-    float f[8];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(w[i] << 16) / s;
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) / s;
+// Per-tensor e4m3 quantiser of the float32 intermediate: code = e4m3 of the
+// IEEE float32 quotient a / s (round to nearest even, saturated at +-448),
+// s = amax / 448.  The quotient is formed from r = 1/s (one IEEE division
+// per thread) and two remainder corrections by fused multiply-add: with r
+// correctly rounded, the first correction leaves the quotient within one
+// ulp and the second returns the correctly rounded quotient (Markstein's
+// theorem), provided nothing under- or overflows.  A scale below the normal
+// range is brought into it by multiplying s and every a by 2^64 (exact, and
+// the quotient is unchanged; s <= FLT_MAX/448 keeps r normal at the top);
+// quotients small enough to lose exactness in the corrections (below
+// 2^-100) quantise to zero either way.  The corrections turn a -0 quotient
+// into +0, so the sign is taken from a (s > 0): a zero quotient keeps the
+// sign an IEEE division gives it.  Everything here is uniform across the
+// wavefront except a, so the per-value path has no branch.
+struct ActQuant {
+    float pre, s, r;
+    __device__ __forceinline__ explicit ActQuant(float scale) {
+        const bool sub = scale < 1.17549435e-38f;
+        pre = sub ? 18446744073709551616.0f : 1.0f;  // 2^64
+        s = scale * pre;
+        r = 1.0f / s;
     }
-    uint2 r;
-    r.x = pack_fp8x4(f[0], f[1], f[2], f[3]);
-    r.y = pack_fp8x4(f[4], f[5], f[6], f[7]);
-    return r;
-}
+    __device__ __forceinline__ float quot(float a0) const {
+        const float a = a0 * pre;
+        float q = a * r;
+        float e = __builtin_fmaf(-q, s, a);
+        q = __builtin_fmaf(e, r, q);
+        e = __builtin_fmaf(-q, s, a);
+        return __builtin_copysignf(__builtin_fmaf(e, r, q), a);
+    }
+    __device__ __forceinline__ float sat(float a) const { return __builtin_amdgcn_fmed3f(quot(a), -448.0f, 448.0f); }
+    // 16 float32 values (four 16-byte chunks) -> 16 e4m3 codes
+    __device__ __forceinline__ uint4 codes16(const uint4& v0, const uint4& v1, const uint4& v2,
+                                             const uint4& v3) const {
+        return uint4{pack4(v0), pack4(v1), pack4(v2), pack4(v3)};
+    }
+    __device__ __forceinline__ uint32_t pack4(const uint4& v) const {
+        return pack_fp8x4(sat(__uint_as_float(v.x)), sat(__uint_as_float(v.y)), sat(__uint_as_float(v.z)),
+                          sat(__uint_as_float(v.w)));
+    }
+};
 
 __device__ __forceinline__ float act_scale_from_amax(const float* amax) {
     float a = *amax;
@@ -137,17 +164,17 @@ __device__ __forceinline__ void amax_publish(float m, float* dst) {
 constexpr int kDecThreads = 256;
 constexpr int kDecSpan = 256;  // bytes of each row per step
 
-// AQ: the DOWN operand is already e4m3 (quantised once by quant_act_kernel)
+// AQ: the DOWN operand is already e4m3 (quantised once by quant_act_kernel);
+// otherwise an e4m3 DOWN reads the float32 intermediate and quantises it on load
 template <int KIND, int DT, bool AQ>
 struct DecodeTokens {
-    static constexpr bool kBf16Act = KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3 && !AQ;
+    static constexpr bool kF32Act = KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3 && !AQ;
     // one 16-byte MFMA operand chunk of the token rows for load u of a step
-    __device__ static __forceinline__ uint4 load(const char* brow, size_t step_off, int u, float qs) {
-        if constexpr (kBf16Act) {
-            // act is bf16: 16 elements = 32 bytes, quantised on load
-            const uint4* p = reinterpret_cast<const uint4*>(brow + 2 * (step_off + u * 64));
-            uint2 lo = quant8(p[0], qs), hi = quant8(p[1], qs);
-            return uint4{lo.x, lo.y, hi.x, hi.y};
+    __device__ static __forceinline__ uint4 load(const char* brow, size_t step_off, int u, const ActQuant& q) {
+        if constexpr (kF32Act) {
+            // act is float32: 16 elements = 64 bytes, quantised on load
+            const uint4* p = reinterpret_cast<const uint4*>(brow + 4 * (step_off + u * 64));
+            return q.codes16(p[0], p[1], p[2], p[3]);
         } else {
             return *reinterpret_cast<const uint4*>(brow + step_off + u * 64);
         }
@@ -220,9 +247,10 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
             scale = qs * g.w_scale[e];
         }
     }
+    const ActQuant quant(qs);
     // token-row byte stride and the lane's offset inside a step
-    const size_t brow_bytes = Tok::kBf16Act ? (size_t)K * 2 : rowb;
-    const int blane = lg * 16;  // in operand bytes (fp8 act: in elements, scaled x2 inside the loader)
+    const size_t brow_bytes = Tok::kF32Act ? (size_t)K * 4 : rowb;
+    const int blane = lg * 16;  // in operand bytes (float32 act: in elements, scaled x4 inside the loader)
 
     extern __shared__ f32x4 red[];  // [4 waves][G*T tiles][NT][64 lanes]
     float amax = 0.0f;
@@ -236,7 +264,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
             const int p = g.sorted[base + r];
             const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
             brow[c] = reinterpret_cast<const char*>(g.a) + (size_t)src * brow_bytes +
-                      (Tok::kBf16Act ? 2 * blane : blane);
+                      (Tok::kF32Act ? 4 * blane : blane);
         }
 
         f32x4 acc[G][T][NT];
@@ -260,7 +288,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
             for (int c = 0; c < NT; ++c)
                 if (c < ntiles)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) b[c][u] = Tok::load(brow[c], soff, u, qs);
+                    for (int u = 0; u < 4; ++u) b[c][u] = Tok::load(brow[c], soff, u, quant);
         };
 
         int s = wave;
@@ -337,6 +365,17 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
                     for (int v = 0; v < 4; ++v) o[v] = silu(gs[v]) * us[v];
                     const int n = n0 + gi * 32 + 16 * q + 4 * lg;
                     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.c) + (size_t)p * I + n) = o;
+                } else if (r < cnt && DT == MOE_FP8_E4M3) {
+                    // the e4m3 layer keeps its intermediate in float32 until it is quantised
+                    const int p = g.sorted[base + r];
+                    f32x4 o;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        o[v] = silu(gs[v] * scale) * (us[v] * scale);
+                        amax = fmaxf(amax, fabsf(o[v]));
+                    }
+                    const int n = n0 + gi * 32 + 16 * q + 4 * lg;
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.c) + (size_t)p * I + n) = o;
                 } else if (r < cnt) {
                     const int p = g.sorted[base + r];
                     float o[4];
@@ -345,12 +384,6 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_kernel(GemmArgs g) {
                     uint2 pk;
                     pk.x = pack_bf2(o[0], o[1]);
                     pk.y = pack_bf2(o[2], o[3]);
-                    if constexpr (DT == MOE_FP8_E4M3) {
-                        amax = fmaxf(amax, fabsf(bf2f(pk.x & 0xffff)));
-                        amax = fmaxf(amax, fabsf(bf2f(pk.x >> 16)));
-                        amax = fmaxf(amax, fabsf(bf2f(pk.y & 0xffff)));
-                        amax = fmaxf(amax, fabsf(bf2f(pk.y >> 16)));
-                    }
                     const int n = n0 + gi * 32 + 16 * q + 4 * lg;
                     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * I + n) = pk;
                 }
@@ -431,7 +464,9 @@ __global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
     const char* asrc[kAChunks];
     const char* bsrc[kBChunks];
     int adst[kAChunks], bdst[kBChunks];
-    const bool a_is_bf16_act = (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) && !g.act_q8;
+    // an e4m3 DOWN reads the float32 intermediate and quantises it on load
+    const bool a_is_f32_act = (KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3) && !g.act_q8;
+    const ActQuant quant(qs);
 #pragma unroll
     for (int q = 0; q < kAChunks; ++q) {
         int id = tid + q * kPreThreads;
@@ -442,8 +477,8 @@ __global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
             asrc[q] = nullptr;
         } else if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
             asrc[q] = reinterpret_cast<const char*>(g.a) + (size_t)(p / g.topk) * K * kElem + cc * 16;
-        } else if (a_is_bf16_act) {
-            asrc[q] = reinterpret_cast<const char*>(g.a) + (size_t)p * K * 2 + cc * 32;
+        } else if (a_is_f32_act) {
+            asrc[q] = reinterpret_cast<const char*>(g.a) + (size_t)p * K * 4 + cc * 64;
         } else {
             asrc[q] = reinterpret_cast<const char*>(g.a) + (size_t)p * K * kElem + cc * 16;
         }
@@ -464,10 +499,9 @@ __global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
         for (int q = 0; q < kAChunks; ++q) {
             if (!asrc[q]) {
                 ra[q] = uint4{0, 0, 0, 0};
-            } else if (a_is_bf16_act) {
-                const uint4* s = reinterpret_cast<const uint4*>(asrc[q] + (size_t)k0 * 2);
-                uint2 lo = quant8(s[0], qs), hi = quant8(s[1], qs);
-                ra[q] = uint4{lo.x, lo.y, hi.x, hi.y};
+            } else if (a_is_f32_act) {
+                const uint4* s = reinterpret_cast<const uint4*>(asrc[q] + (size_t)k0 * 4);
+                ra[q] = quant.codes16(s[0], s[1], s[2], s[3]);
             } else {
                 ra[q] = *reinterpret_cast<const uint4*>(asrc[q] + (size_t)k0 * kElem);
             }
@@ -561,10 +595,15 @@ __global__ void __launch_bounds__(kPreThreads) gemm_prefill_kernel(GemmArgs g) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     float gv = acc[i][j][v] * scale, uv = acc[i][j + 2][v] * scale;
-                    uint16_t h = f2bf(silu(gv) * uv);
-                    if constexpr (DT == MOE_FP8_E4M3) amax = fmaxf(amax, fabsf(bf2f(h)));
+                    const float o = silu(gv) * uv;
                     const int n = n0 + wn * 32 + 16 * j + lr;
-                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * I + n] = h;
+                    if constexpr (DT == MOE_FP8_E4M3) {
+                        // float32 intermediate until it is quantised
+                        amax = fmaxf(amax, fabsf(o));
+                        reinterpret_cast<float*>(g.c)[(size_t)p * I + n] = o;
+                    } else {
+                        reinterpret_cast<uint16_t*>(g.c)[(size_t)p * I + n] = f2bf(o);
+                    }
                 }
             } else {
 #pragma unroll
@@ -879,9 +918,14 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
                         uv *= scale;
                     }
                     const int n = n0 + wn * (C::WTN / 2) + 32 * j + (lane & 31);
-                    const uint16_t h = f2bf(silu(gv) * uv);
-                    if constexpr (DT == MOE_FP8_E4M3) amax = fmaxf(amax, fabsf(bf2f(h)));
-                    reinterpret_cast<uint16_t*>(g.c)[(size_t)p * I + n] = h;
+                    const float o = silu(gv) * uv;
+                    if constexpr (DT == MOE_FP8_E4M3) {
+                        // float32 intermediate until it is quantised
+                        amax = fmaxf(amax, fabsf(o));
+                        reinterpret_cast<float*>(g.c)[(size_t)p * I + n] = o;
+                    } else {
+                        reinterpret_cast<uint16_t*>(g.c)[(size_t)p * I + n] = f2bf(o);
+                    }
                 }
             } else {
 #pragma unroll
@@ -945,16 +989,27 @@ static hipError_t launch_prefill2(const GemmArgs& a, int64_t cap, int E, hipStre
 // bytes of the group's 64 weight rows and of the pass's 16*NT token rows.
 // No other wavefront touches a ring, so the main loop has no barrier: each
 // wave waits on its own copies with vmcnt.
+//
+// TQ (e4m3 down projection over the float32 intermediate, one token tile):
+// the token rows do not go through the ring.  Each lane loads the float32
+// values of its MFMA operand (two 64-byte pieces of its token row per step)
+// into registers two steps ahead and quantises them to e4m3 codes just
+// before the step's MFMAs, so the intermediate is read once per row group
+// at four bytes per value and never written back as codes.  The loads of
+// step j+2 are issued after the wait that retires step j's weight copies,
+// which keeps that wait exact: the weight copies of step j+1 are the only
+// younger vector-memory operations, and the compiler's own wait before the
+// token registers of step j asks for no more than that one.
 
 constexpr int kRingSB = 128;  // bytes of every row per step
 
-template <int NT, int G, int KD>
+template <int NT, int G, int KD, bool TQ = false>
 struct DecRing {
-    static constexpr int WInstr = 64 * kRingSB / 1024;       // copy instructions for the weight rows
-    static constexpr int TInstr = NT * 16 * kRingSB / 1024;  // ... and for the token rows
+    static constexpr int WInstr = 64 * kRingSB / 1024;                   // copy instructions for the weight rows
+    static constexpr int TInstr = TQ ? 0 : NT * 16 * kRingSB / 1024;     // ... and for the token rows
     static constexpr int Instr = WInstr + TInstr;
-    static constexpr int TokOff = 64 * kRingSB;              // token rows follow the weight rows
-    static constexpr int Stage = (64 + 16 * NT) * kRingSB;
+    static constexpr int TokOff = 64 * kRingSB;                          // token rows follow the weight rows
+    static constexpr int Stage = (64 + (TQ ? 0 : 16 * NT)) * kRingSB;
     static constexpr int Ring = 4 * KD * Stage;
     static constexpr int Red = 4 * G * 4 * NT * 64 * 16;     // [4 waves][G*4 tiles][NT][64 lanes] f32x4
     static constexpr int Lds = Ring > Red ? Ring : Red;
@@ -976,9 +1031,10 @@ __device__ __forceinline__ void ring_wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int KIND, int DT, int NT, int G, int KD>
+template <int KIND, int DT, int NT, int G, int KD, bool TQ>
 __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs g) {
-    using R = DecRing<NT, G, KD>;
+    using R = DecRing<NT, G, KD, TQ>;
+    static_assert(!TQ || (NT == 1 && KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3), "TQ: e4m3 DOWN, one token tile");
     constexpr int kElem = Opnd<DT>::kElemBytes;
     constexpr int T = 4;  // 16-row tiles per group
     extern __shared__ __attribute__((aligned(1024))) char ring_lds[];
@@ -1018,13 +1074,16 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
         woff[i] = (size_t)row * rowb + ring_swz(dpc, ri) * 16;
     }
 
-    float scale = 1.0f;
+    float scale = 1.0f, qs = 1.0f;
     if constexpr (DT == MOE_FP8_E4M3) {
-        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU)
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
             scale = g.a_scale[0] * g.w_scale[e];
-        else
-            scale = act_scale_from_amax(g.a_scale) * g.w_scale[e];
+        } else {
+            qs = act_scale_from_amax(g.a_scale);
+            scale = qs * g.w_scale[e];
+        }
     }
+    const ActQuant quant(qs);
 
     char* ring = ring_lds + wave * (KD * R::Stage);
     f32x4* red = reinterpret_cast<f32x4*>(ring_lds);  // after the main loop only
@@ -1035,16 +1094,22 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
         // token-row sources of this lane's copies (rows past the expert's
         // count repeat its last row; their products are not used)
         size_t toff[NT][2];
+        const char* trow = nullptr;  // TQ: this lane's float32 token row, at its lane group's 64 bytes
+        if constexpr (TQ) {
+            const int p = g.sorted[base + min(pass + lr, cnt - 1)];
+            trow = reinterpret_cast<const char*>(g.a) + (size_t)p * K * 4 + 64 * lg;
+        } else {
 #pragma unroll
-        for (int c = 0; c < NT; ++c)
+            for (int c = 0; c < NT; ++c)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int rr = 16 * c + 8 * h + drow;
-                const int r = min(pass + rr, cnt - 1);
-                const int p = g.sorted[base + r];
-                const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
-                toff[c][h] = (size_t)src * rowb + ring_swz(dpc, rr) * 16;
-            }
+                for (int h = 0; h < 2; ++h) {
+                    const int rr = 16 * c + 8 * h + drow;
+                    const int r = min(pass + rr, cnt - 1);
+                    const int p = g.sorted[base + r];
+                    const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
+                    toff[c][h] = (size_t)src * rowb + ring_swz(dpc, rr) * 16;
+                }
+        }
 
         auto issue = [&](int j) {
             const int s = wave + 4 * j;
@@ -1055,11 +1120,24 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
             const char* wsrc = wexp + gi * gstride + (size_t)ks * kRingSB;
 #pragma unroll
             for (int i = 0; i < R::WInstr; ++i) lds_dma16_nt(wsrc + woff[i], st + i * 1024);
-            const char* tsrc = reinterpret_cast<const char*>(g.a) + (size_t)ks * kRingSB;
+            if constexpr (!TQ) {
+                const char* tsrc = reinterpret_cast<const char*>(g.a) + (size_t)ks * kRingSB;
 #pragma unroll
-            for (int c = 0; c < NT; ++c)
+                for (int c = 0; c < NT; ++c)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) lds_dma16(tsrc + toff[c][h], st + R::TokOff + (2 * c + h) * 1024);
+                    for (int h = 0; h < 2; ++h) lds_dma16(tsrc + toff[c][h], st + R::TokOff + (2 * c + h) * 1024);
+            }
+        };
+        // TQ: the float32 operand values of step j (elements 16 lg.. and 64 + 16 lg.. of the
+        // step's 128, i.e. logical chunks lg and lg + 4 of the weight rows)
+        auto tload = [&](uint4 (&b)[8], int j) {
+            const int ks = ks0 + (wave + 4 * j) % nks;
+            const uint4* src = reinterpret_cast<const uint4*>(trow + (size_t)ks * (4 * kRingSB));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                b[u] = src[u];
+                b[4 + u] = src[16 + u];
+            }
         };
 
         f32x4 acc[G][T][NT];
@@ -1070,15 +1148,37 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
 #pragma unroll
                 for (int c = 0; c < NT; ++c) acc[gi][t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+        uint4 tb[TQ ? 2 : 1][TQ ? 8 : 1];
+        if constexpr (TQ) {
+            // token values of steps 0 and 1 before the first weight copies (a
+            // wave with fewer steps loads step 0 again: any step index >= 0
+            // names an in-bounds K step of this workgroup's range)
+            tload(tb[0], 0);
+            tload(tb[1], nw > 1 ? 1 : 0);
+        }
 #pragma unroll
         for (int j = 0; j < KD - 1; ++j)
             if (j < nw) issue(j);
-        for (int j = 0; j < nw; ++j) {
+        // one step of the ring; TQ: tbuf holds step j's token values and is
+        // refilled with step j + 2's (two buffers in fixed roles, so no
+        // register copy makes the compiler wait on the loads just issued)
+        auto step = [&](int j, uint4 (&tbuf)[TQ ? 8 : 1]) {
             if (j + KD - 1 < nw) {
                 issue(j + KD - 1);
                 ring_wait_vm<(KD - 1) * R::Instr>();
             } else {
                 ring_wait_vm<0>();
+            }
+            // TQ: every vector-memory operation older than the weight copies
+            // just issued has completed, the token loads of step j included
+            uint4 tq0 = {0, 0, 0, 0}, tq1 = {0, 0, 0, 0};
+            if constexpr (TQ) {
+                tq0 = quant.codes16(tbuf[0], tbuf[1], tbuf[2], tbuf[3]);
+                tq1 = quant.codes16(tbuf[4], tbuf[5], tbuf[6], tbuf[7]);
+                // unconditional (the last steps reload step nw-1, unused): a
+                // conditional refill would merge two register states and the
+                // copies that merge needs would wait on these very loads
+                tload(tbuf, min(j + 2, nw - 1));
             }
             const char* st = ring + (j % KD) * R::Stage;
             const int gi = (wave + 4 * j) / nks;
@@ -1096,14 +1196,20 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
                         a0[t] = *reinterpret_cast<const uint4*>(rp + ((lg ^ sw) << 4));
                         a1[t] = *reinterpret_cast<const uint4*>(rp + (((lg + 4) ^ sw) << 4));
                     }
+                    if constexpr (TQ) {
 #pragma unroll
-                    for (int c = 0; c < NT; ++c) {
-                        if (c < ntiles) {
-                            const char* bp = st + R::TokOff + (16 * c + lr) * kRingSB;
-                            const uint4 b0 = *reinterpret_cast<const uint4*>(bp + ((lg ^ sw) << 4));
-                            const uint4 b1 = *reinterpret_cast<const uint4*>(bp + (((lg + 4) ^ sw) << 4));
+                        for (int t = 0; t < T; ++t) acc[gg][t][0] = mfma_f8_16x16x128(a0[t], a1[t], tq0, tq1, acc[gg][t][0]);
+                    } else {
 #pragma unroll
-                            for (int t = 0; t < T; ++t) acc[gg][t][c] = mfma_f8_16x16x128(a0[t], a1[t], b0, b1, acc[gg][t][c]);
+                        for (int c = 0; c < NT; ++c) {
+                            if (c < ntiles) {
+                                const char* bp = st + R::TokOff + (16 * c + lr) * kRingSB;
+                                const uint4 b0 = *reinterpret_cast<const uint4*>(bp + ((lg ^ sw) << 4));
+                                const uint4 b1 = *reinterpret_cast<const uint4*>(bp + (((lg + 4) ^ sw) << 4));
+#pragma unroll
+                                for (int t = 0; t < T; ++t)
+                                    acc[gg][t][c] = mfma_f8_16x16x128(a0[t], a1[t], b0, b1, acc[gg][t][c]);
+                            }
                         }
                     }
                 } else {
@@ -1126,6 +1232,16 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
                     }
                 }
             }
+        };
+        if constexpr (TQ) {
+            int j = 0;
+            for (; j + 1 < nw; j += 2) {
+                step(j, tb[0]);
+                step(j + 1, tb[1]);
+            }
+            if (j < nw) step(j, tb[0]);
+        } else {
+            for (int j = 0; j < nw; ++j) step(j, tb[0]);
         }
 
         // every wave is done with its ring: the reduction area aliases it
@@ -1154,20 +1270,21 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
                     gs += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
                     us += red[((w * G * T + gi * T + q + 2) * NT + c) * 64 + lane];
                 }
-                float o[4];
+                f32x4 o;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) o[v] = silu(gs[v] * scale) * (us[v] * scale);
-                uint2 pk;
-                pk.x = pack_bf2(o[0], o[1]);
-                pk.y = pack_bf2(o[2], o[3]);
-                if constexpr (DT == MOE_FP8_E4M3) {
-                    amax = fmaxf(amax, fabsf(bf2f(pk.x & 0xffff)));
-                    amax = fmaxf(amax, fabsf(bf2f(pk.x >> 16)));
-                    amax = fmaxf(amax, fabsf(bf2f(pk.y & 0xffff)));
-                    amax = fmaxf(amax, fabsf(bf2f(pk.y >> 16)));
-                }
                 const int n = n0 + gi * 32 + 16 * q + 4 * lg;
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * I + n) = pk;
+                if constexpr (DT == MOE_FP8_E4M3) {
+                    // the e4m3 layer keeps its intermediate in float32 until it is quantised
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(o[v]));
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.c) + (size_t)p * I + n) = o;
+                } else {
+                    uint2 pk;
+                    pk.x = pack_bf2(o[0], o[1]);
+                    pk.y = pack_bf2(o[2], o[3]);
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * I + n) = pk;
+                }
             } else {
                 f32x4 ys = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1189,17 +1306,17 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
     if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) amax_publish(amax, g.c_amax);
 }
 
-template <int KIND, int DT, int NT, int G, int KD>
+template <int KIND, int DT, int NT, int G, int KD, bool TQ = false>
 static hipError_t launch_decode_ring(const GemmArgs& a, int nslots, hipStream_t s) {
-    using R = DecRing<NT, G, KD>;
+    using R = DecRing<NT, G, KD, TQ>;
     const int rows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 * G : 64 * G;  // output columns per workgroup
     const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
     // LDS above the default dynamic limit must be requested once per kernel
     static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_ring_kernel<KIND, DT, NT, G, KD>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_ring_kernel<KIND, DT, NT, G, KD, TQ>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, R::Lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemm_decode_ring_kernel<KIND, DT, NT, G, KD>), dim3(ncols / rows, nslots, a.ksplit),
+    hipLaunchKernelGGL((gemm_decode_ring_kernel<KIND, DT, NT, G, KD, TQ>), dim3(ncols / rows, nslots, a.ksplit),
                        dim3(kDecThreads), R::Lds, s, a);
     return hipGetLastError();
 }
@@ -1281,18 +1398,27 @@ GemmPath choose_gemm_path(const GemmCall& g) {
 template <int KIND, int DT, int NT, int G, bool AQ>
 static hipError_t launch_decode_ntga(const GemmArgs& a, int nslots, hipStream_t s) {
     // operands whose rows the MFMAs read as stored go through the LDS ring
-    // kernel; f32 calls and a bf16 intermediate quantised on load do not
-    constexpr bool kRing = DT != MOE_F32 && !(KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3 && !AQ);
+    // kernel, and so does an e4m3 DOWN over the float32 intermediate with one
+    // token tile (its token values through registers, quantised on load);
+    // f32 calls and an e4m3 DOWN with more token tiles take the register kernel
+    constexpr bool kF32Act = KIND == MOE_GEMM_DOWN && DT == MOE_FP8_E4M3 && !AQ;
+    constexpr bool kRing = DT != MOE_F32 && (!kF32Act || NT == 1);
     // (two stages per ring: measured as fast as three on every decode
     // workload, and it leaves LDS for a second workgroup at one token tile)
     if constexpr (kRing) {
-        return launch_decode_ring<KIND, DT, NT, G, 2>(a, nslots, s);
+        return launch_decode_ring<KIND, DT, NT, G, 2, kF32Act>(a, nslots, s);
     } else {
         const int rows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 * G : 64 * G;  // output columns per workgroup
         const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
-        const size_t lds = sizeof(f32x4) * 4 * G * 4 * NT * 64;
+        constexpr size_t kLds = sizeof(f32x4) * 4 * G * 4 * NT * 64;  // the cross-wavefront reduction
+        static_assert(kLds <= 160 * 1024, "LDS");
+        // LDS above the default dynamic limit must be requested once per kernel
+        static const hipError_t attr =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_kernel<KIND, DT, NT, G, AQ>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+        if (attr != hipSuccess) return attr;
         hipLaunchKernelGGL((gemm_decode_kernel<KIND, DT, NT, G, AQ>), dim3(ncols / rows, nslots, a.ksplit),
-                           dim3(kDecThreads), lds, s, a);
+                           dim3(kDecThreads), kLds, s, a);
         return hipGetLastError();
     }
 }
@@ -1343,18 +1469,29 @@ static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_es
     return launch_decode_ntg<KIND, DT, NT, 1>(a, nslots, s);
 }
 
+// Token tiles of 16 rows per pass of the decode kernels: a high quantile of
+// the rows per expert under uniform routing.
+static int decode_token_tiles(int M, int topk, int E) {
+    const double avg = (double)M * topk / E;
+    const double hi = avg + 3.0 * __builtin_sqrt(avg) + 1.0;
+    return hi <= 16.0 ? 1 : hi <= 32.0 ? 2 : 4;
+}
+
 template <int KIND, int DT>
 static hipError_t launch_decode(const GemmArgs& a, int M, int topk, int E, hipStream_t s) {
     const long P = (long)M * topk;
     const int nslots = (int)(P < E ? P : E);
-    // expected active experts and a high quantile of rows per expert under
-    // uniform routing pick the token tiles per pass
-    const double avg = (double)P / E;
-    const double hi = avg + 3.0 * __builtin_sqrt(avg) + 1.0;
     const long active_est = nslots;
-    if (hi <= 16.0) return launch_decode_nt<KIND, DT, 1>(a, nslots, active_est, s);
-    if (hi <= 32.0) return launch_decode_nt<KIND, DT, 2>(a, nslots, active_est, s);
+    const int nt = decode_token_tiles(M, topk, E);
+    if (nt == 1) return launch_decode_nt<KIND, DT, 1>(a, nslots, active_est, s);
+    if (nt == 2) return launch_decode_nt<KIND, DT, 2>(a, nslots, active_est, s);
     return launch_decode_nt<KIND, DT, 4>(a, nslots, active_est, s);
+}
+
+bool fp8_down_quantises_on_load(int M, int topk, int E, int N, int K, int block_m) {
+    GemmCall probe{MOE_GEMM_DOWN, MOE_FP8_E4M3, nullptr, nullptr, nullptr, nullptr, {}, M, topk, E, N, K, block_m,
+                   nullptr, nullptr};
+    return choose_gemm_path(probe) == GemmPath::kDecode && decode_token_tiles(M, topk, E) == 1;
 }
 
 template <int KIND, int DT>
@@ -1431,26 +1568,30 @@ namespace moe {
 
 // ------------------------------------------------------- fp8 intermediate
 //
-// The fused layer quantises the bf16 intermediate once (value / (amax/448),
-// IEEE division, round to nearest even, as quant8 does on load in the
-// stand-alone down GEMM) so the down GEMM reads e4m3 codes directly.
-// Each thread converts 16 elements.
-__global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restrict__ act,
+// e4m3 codes of the float32 intermediate, s = amax/448 (ActQuant), for the
+// down projections that read codes (tile kernels with many rows per expert,
+// where every weight tile would otherwise re-read and re-quantise the
+// four-byte rows).
+__global__ void __launch_bounds__(256) quant_act_kernel(const float* __restrict__ act,
                                                         const float* __restrict__ amax, uint8_t* __restrict__ q,
-                                                        size_t n16) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n16) return;
-    const float s = act_scale_from_amax(amax);
-    const uint4* p = reinterpret_cast<const uint4*>(act) + 2 * i;
-    const uint2 lo = quant8(p[0], s), hi = quant8(p[1], s);
-    reinterpret_cast<uint4*>(q)[i] = uint4{lo.x, lo.y, hi.x, hi.y};
+                                                        size_t n4) {
+    const ActQuant quant(act_scale_from_amax(amax));
+    // each lane converts 4 consecutive values per round: a wavefront reads
+    // 1 KB and writes 256 contiguous bytes per instruction
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(act) + i);
+        reinterpret_cast<uint32_t*>(q)[i] = quant.pack4(uint4{v.x, v.y, v.z, v.w});
+    }
 }
 
 hipError_t launch_quant_act(const void* act, const float* amax, void* q, size_t n, hipStream_t s) {
-    const size_t n16 = n / 16;
-    if (n16 == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(act), amax, static_cast<uint8_t*>(q), n16);
+    const size_t n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    const size_t blocks = (n4 + 255) / 256;
+    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
+                       static_cast<const float*>(act), amax, static_cast<uint8_t*>(q), n4);
     return hipGetLastError();
 }
 

@@ -28,8 +28,10 @@ bool valid_block_m(int32_t b) { return b == 1 || b == 16 || b == 32 || b == 64 |
 
 size_t elem_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : d == MOE_BF16 ? 2 : 1; }
 
-// bytes of the intermediate rows (act, y): f32 for the f32 path, bf16 otherwise
+// bytes of an element of y: f32 for the f32 path, bf16 otherwise
 size_t inter_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : 2; }
+// ... and of act: the e4m3 layer keeps it in float32 until it is quantised
+size_t act_bytes(moe_dtype d) { return d == MOE_BF16 ? 2 : 4; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -65,7 +67,8 @@ struct FusedLayout {
     moe_align_bufs al;
     void* act;
     void* y;
-    void* act_q;  // fp8: e4m3 codes of act
+    bool q_on_load;  // fp8: the DOWN kernel quantises the float32 act on load
+    void* act_q;     // fp8 otherwise: e4m3 codes of act
     float* ypart;
     float* amax;
 };
@@ -85,9 +88,10 @@ FusedLayout fused_layout(char* ws, moe_dtype dtype, int32_t M, int32_t E, int32_
     L.al.active_experts = c.take<int32_t>(P < E ? P : E);
     L.al.num_active = c.take<int32_t>(1);
     L.amax = c.take<float>(1);
-    L.act = c.take<char>((size_t)P * I * inter_bytes(dtype));
+    L.act = c.take<char>((size_t)P * I * act_bytes(dtype));
     L.y = c.take<char>((size_t)P * H * inter_bytes(dtype));
-    L.act_q = dtype == MOE_FP8_E4M3 ? c.take<char>((size_t)P * I) : nullptr;
+    L.q_on_load = dtype == MOE_FP8_E4M3 && fp8_down_quantises_on_load(M, topk, E, H, I, L.block_m);
+    L.act_q = (dtype == MOE_FP8_E4M3 && !L.q_on_load) ? c.take<char>((size_t)P * I) : nullptr;
     L.ksplit = down_ksplit(dtype, M, topk, E, H, I, L.block_m);
     L.ypart = L.ksplit > 1 ? c.take<float>((size_t)L.ksplit * P * H) : nullptr;
     L.bytes = c.off;
@@ -245,9 +249,12 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
     GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, x, x_scale, w1, w1_scale, L.al, M, topk, E, 2 * I, H,
                 L.block_m, L.act, fp8 ? L.amax : nullptr};
     if (launch_grouped_gemm(g1, s) != hipSuccess) return MOE_ERR_HIP;
-    if (fp8 && launch_quant_act(L.act, L.amax, L.act_q, (size_t)M * topk * I, s) != hipSuccess) return MOE_ERR_HIP;
-    GemmCall g2{MOE_GEMM_DOWN, dtype, fp8 ? L.act_q : L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E,
-                H, I, L.block_m, L.y, nullptr, L.ksplit, L.ypart, fp8};
+    // e4m3: the down kernel quantises the float32 intermediate as it loads it,
+    // or (tile kernels) reads codes quantised once here
+    const bool codes = fp8 && !L.q_on_load;
+    if (codes && launch_quant_act(L.act, L.amax, L.act_q, (size_t)M * topk * I, s) != hipSuccess) return MOE_ERR_HIP;
+    GemmCall g2{MOE_GEMM_DOWN, dtype, codes ? L.act_q : L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E,
+                H, I, L.block_m, L.y, nullptr, L.ksplit, L.ypart, codes};
     if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
     if (L.ksplit > 1) return hip_status(launch_combine_partials(L.ypart, L.ksplit, wts, M, topk, H, inter, out, s));
     return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));

@@ -44,7 +44,7 @@ struct GemmCall {
     float* c_amax;
     int ksplit = 1;         // decode DOWN: split of K across workgroups
     float* cpart = nullptr;  // with ksplit > 1: float32 partials [ksplit][P][N] instead of c
-    bool act_q8 = false;     // fp8 DOWN: a already holds e4m3 codes (quantised with amax/448)
+    bool act_q8 = false;     // fp8 DOWN: a holds e4m3 codes (quantised with amax/448), not the float32 act
 };
 
 // Kernel family chosen for a call (decode for few rows per expert, or when
@@ -58,7 +58,13 @@ hipError_t launch_grouped_gemm(const GemmCall& g, hipStream_t s);
 // already has enough workgroups, or when the prefill kernel serves the call).
 int down_ksplit(moe_dtype dtype, int M, int topk, int E, int N, int K, int block_m);
 
-// e4m3 codes of n bf16 intermediate values (n a multiple of 16), scale amax/448.
+// Whether an e4m3 DOWN call of these sizes runs a kernel that reads the
+// float32 intermediate and quantises it on load (decode kernel, one token
+// tile); otherwise the fused layer quantises the intermediate once
+// (launch_quant_act) and the DOWN kernel reads the codes.
+bool fp8_down_quantises_on_load(int M, int topk, int E, int N, int K, int block_m);
+
+// e4m3 codes of n float32 intermediate values (n a multiple of 16), scale amax/448.
 hipError_t launch_quant_act(const void* act, const float* amax, void* q, size_t n, hipStream_t s);
 
 hipError_t launch_combine_partials(const float* ypart, int ksplit, const float* w, int M, int topk, int H,

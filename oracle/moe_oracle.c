@@ -99,11 +99,19 @@ uint8_t oracle_e4m3_encode(double v) {
     return sign | (uint8_t)(ef << 3) | (uint8_t)(n - 8.0);
 }
 
+/* oracle_e4m3_decode of every code, filled once when the library is loaded
+ * (the same function, looked up instead of recomputed per element). */
+static double e4m3_value[256];
+
+__attribute__((constructor)) static void fill_e4m3_table(void) {
+    for (int c = 0; c < 256; ++c) e4m3_value[c] = oracle_e4m3_decode((uint8_t)c);
+}
+
 static double elem(int dtype, const void* base, int64_t i) {
     switch (dtype) {
         case OR_F32: return (double)((const float*)base)[i];
         case OR_BF16: return oracle_bf16_decode(((const uint16_t*)base)[i]);
-        default: return oracle_e4m3_decode(((const uint8_t*)base)[i]);
+        default: return e4m3_value[((const uint8_t*)base)[i]];
     }
 }
 

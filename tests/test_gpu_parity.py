@@ -97,7 +97,7 @@ ALIGN_CASES = [("uniform", 64, 8, 2), ("uniform", 4096, 8, 2), ("zipf", 4096, 8,
 
 
 @pytest.mark.parametrize("kind,M,E,k", ALIGN_CASES)
-@pytest.mark.parametrize("bm", [1, 16, 64, 128])
+@pytest.mark.parametrize("bm", [1, 16, 32, 64, 128, 256])
 def test_align(dev, kind, M, E, k, bm):
     import moe_layer_topk_amd as moe
     say(f"align {kind} M={M} E={E} k={k} bm={bm}")
@@ -155,12 +155,12 @@ def test_grouped_gemm(dev, monkeypatch, dtype, E, k, H, I, M, path):
     assert err <= TOL[dtype]
     if dtype == "fp8":
         assert abs(float(amax) - float(act.float().abs().max())) == 0.0
-    # DOWN on a generated intermediate (bf16 rows; f32 for the f32 path)
-    if dtype == "f32":
+    # DOWN on a generated intermediate (bf16 rows; float32 for the f32 and e4m3 paths)
+    if dtype in ("f32", "fp8"):
         a_in = normal_f32(seed=5, stream=S_ACT, shape=(P, I), std=0.1, device=dev)
     else:
         a_in = normal_bf16(seed=5, stream=S_ACT, shape=(P, I), std=0.1, device=dev)
-    a_amax = a_in.float().abs().max().reshape(1) if dtype == "fp8" else None
+    a_amax = a_in.abs().max().reshape(1) if dtype == "fp8" else None
     y, _ = moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN, a_in, w["w2"].to(dev), al, M, k, a_scale=a_amax,
                                 w_scale=sc(w["w2_scale"]))
     torch.cuda.synchronize()
@@ -170,11 +170,12 @@ def test_grouped_gemm(dev, monkeypatch, dtype, E, k, H, I, M, path):
     say(f"  down rel err {err:.2e}")
     assert err <= TOL[dtype]
     if dtype == "fp8":
-        # quantise-once path: codes bit-exact against the oracle's encoder, and
-        # the down GEMM over those codes equal to the quantise-on-load GEMM
+        # the codes the down call forms on load, as a tensor: bit-exact against
+        # the oracle's encoder of the float32 quotient; the down GEMM over them
+        # within the bar of the quantise-on-load one
         q = moe.moe_quant_act(a_in, a_amax)
         s32 = np.float32(float(a_amax)) / np.float32(448.0)
-        v = a_in.float().cpu().numpy().ravel() / s32
+        v = a_in.cpu().numpy().ravel() / s32
         want = np.array([oracle.e4m3_encode(float(t)) for t in v], np.uint8)
         assert np.array_equal(q.view(torch.uint8).cpu().numpy().ravel(), want)
         y8, _ = moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN_E4M3_ACT, q, w["w2"].to(dev), al, M, k, a_scale=a_amax,
@@ -183,9 +184,56 @@ def test_grouped_gemm(dev, monkeypatch, dtype, E, k, H, I, M, path):
         err8 = rel_err(y8, yref)
         say(f"  down (e4m3 act) rel err {err8:.2e}")
         assert err8 <= TOL[dtype]
-        if path == "decode":
-            # the same kernel quantises on load or reads the codes: identical sums
-            assert torch.equal(y8, y)
+
+
+def test_fp8_down_quantise_on_load_equals_codes(dev, monkeypatch):
+    """One token tile per expert: the decode ring kernel quantises the float32
+    intermediate on load; fed the codes of moe_quant_act instead, the same
+    kernel computes the same products in the same order (bitwise equal)."""
+    import moe_layer_topk_amd as moe
+    monkeypatch.setenv("MOE_GEMM_PATH", "decode")
+    for (E, k, H, I, M) in [(16, 2, 512, 768, 8), (64, 8, 1024, 2048, 3), (8, 2, 256, 4096, 1)]:
+        say(f"fp8 down on-load vs codes E={E} k={k} H={H} I={I} M={M}")
+        cfg, w, b = _gemm_case("fp8", E, k, H, I, M, seed=3)
+        rid, _ = oracle.route(b["logits"], k)
+        al = moe.moe_align(torch.from_numpy(rid).to(dev), E, 16)
+        a_in = normal_f32(seed=7, stream=S_ACT, shape=(M * k, I), std=0.3, device=dev)
+        amax = a_in.abs().max().reshape(1)
+        y, _ = moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN, a_in, w["w2"].to(dev), al, M, k, a_scale=amax,
+                                    w_scale=w["w2_scale"].to(dev))
+        q = moe.moe_quant_act(a_in, amax)
+        y8, _ = moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN_E4M3_ACT, q, w["w2"].to(dev), al, M, k, a_scale=amax,
+                                     w_scale=w["w2_scale"].to(dev))
+        torch.cuda.synchronize()
+        assert torch.equal(y, y8)
+        yref = oracle.pairs_down("fp8", a_in.cpu(), rid, w["w2"], w["w2_scale"], np.arange(M * k),
+                                 act_amax_value=float(amax))
+        assert rel_err(y, yref) <= TOL["fp8"]
+
+
+def test_quant_act_codes_exhaustive_near_ties(dev):
+    """moe_quant_act against the oracle's encoder on values placed at, just
+    below and just above every e4m3 rounding midpoint (and the saturation
+    edge) for a few scales: the float32 quotient and its rounding decide
+    every code exactly as an IEEE division does."""
+    import moe_layer_topk_amd as moe
+    grid = np.array([oracle.e4m3_decode(c) for c in range(0x7F)])
+    mids = (grid[1:] + grid[:-1]) / 2
+    say("quant_act near ties")
+    for amax in (1.0, 24.875, 3.3e-3, 448.0 * 7.5):
+        s32 = np.float32(amax) / np.float32(448.0)
+        base = np.concatenate([grid, mids, [448.0, 460.0, 463.9, 464.0]]).astype(np.float64) * float(s32)
+        vals = np.concatenate([base, np.nextafter(base, 0), np.nextafter(base, 1e30)])
+        vals = np.concatenate([vals, -vals]).astype(np.float32)
+        vals = np.clip(vals, -amax, amax).astype(np.float32)
+        vals = np.concatenate([vals, np.zeros((-len(vals)) % 16, np.float32)])
+        act = torch.from_numpy(vals).to(dev)
+        q = moe.moe_quant_act(act, torch.tensor([amax], dtype=torch.float32, device=dev))
+        torch.cuda.synchronize()
+        want = np.array([oracle.e4m3_encode(float(np.float32(t) / s32)) for t in vals], np.uint8)
+        got = q.view(torch.uint8).cpu().numpy()
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, [(float(vals[i]), int(got[i]), int(want[i])) for i in bad[:5]]
 
 
 # ----------------------------------------------------------------- combine
@@ -218,21 +266,26 @@ def weights(cfg, dev):
     return _W[cfg]
 
 
-def run_fused(cfg, b, w, dev, topk_ids=None):
+def run_fused(cfg, b, w, dev, topk_ids=None, topk_weights=None):
     import moe_layer_topk_amd as moe
     return moe.fused_moe(b["x"], b["logits"], w["w1"], w["w2"], cfg.topk, x_scale=b["x_scale"],
-                         w1_scale=w["w1_scale"], w2_scale=w["w2_scale"], topk_ids=topk_ids)
+                         w1_scale=w["w1_scale"], w2_scale=w["w2_scale"], topk_ids=topk_ids,
+                         topk_weights=topk_weights)
 
 
 def check_layer(cfg, M, dev, tokens=None, act_amax=None, batch=None):
     w, wh = weights(cfg, dev)
     b = layer_batch(cfg, M, dev) if batch is None else batch
     ids = torch.empty((M, cfg.topk), dtype=torch.int32, device=dev)
-    out = run_fused(cfg, b, w, dev, topk_ids=ids)
+    wts = torch.empty((M, cfg.topk), dtype=torch.float32, device=dev)
+    out = run_fused(cfg, b, w, dev, topk_ids=ids, topk_weights=wts)
     torch.cuda.synchronize()
     bh = {k: (v.cpu() if v is not None else None) for k, v in b.items()}
-    rid, _ = oracle.route(bh["logits"], cfg.topk)
+    rid, rw = oracle.route(bh["logits"], cfg.topk)
     assert np.array_equal(ids.cpu().numpy(), rid)
+    # routing weights of the layer's own routing step (one launch with the
+    # alignment for a few tokens, a separate route kernel otherwise)
+    assert np.abs(wts.cpu().numpy() - rw).max() <= 1e-6
     tok = np.arange(M) if tokens is None else np.asarray(tokens)
     amax = act_amax
     if cfg.dtype == "fp8" and amax is None:
@@ -256,17 +309,32 @@ def test_fused_layer(dev, name, M):
 
 
 def test_fused_layer_full_decode_batch(dev):
-    say("fused mixtral_decode_bf16 M=64 (sampled tokens)")
-    check_layer(CONFIGS["mixtral_decode_bf16"], 64, dev, tokens=[0, 1, 17, 31, 32, 50, 62, 63])
-
-
-SAMPLE = [0, 1, 2, 3, 100, 255]
+    say("fused mixtral_decode_bf16 M=64 (every token)")
+    check_layer(CONFIGS["mixtral_decode_bf16"], 64, dev)
 
 
 @pytest.mark.parametrize("M", [256, 2048])
 def test_fused_finegrained_full_sizes(dev, M):
-    say(f"fused finegrained_bf16 M={M} (sampled tokens)")
-    check_layer(CONFIGS["finegrained_bf16"], M, dev, tokens=[t for t in SAMPLE + [M - 2, M - 1] if t < M])
+    say(f"fused finegrained_bf16 M={M} (every token)")
+    check_layer(CONFIGS["finegrained_bf16"], M, dev)
+
+
+def tile_tokens(logits, E, k, block_m, rows=(0, 5, 13, 37, 70, 101, 127)):
+    """Tokens whose pairs reach every row tile of the tile kernels' grid: for
+    each block_m-row tile of the alignment, the pairs at the listed row
+    offsets (both wavefront rows, both lane halves, several accumulator
+    registers) and at the tile's last real row, which covers every expert's
+    last, partial tile."""
+    rid, _ = oracle.route(logits, k)
+    al = oracle.align(rid, E, block_m)
+    tok = set()
+    for e in range(E):
+        c, start = int(al["expert_counts"][e]), int(al["expert_offsets"][e])
+        for t0 in range(0, c, block_m):
+            real = min(block_m, c - t0)
+            for r in [x for x in rows if x < real] + [real - 1]:
+                tok.add(int(al["sorted_ids"][start + t0 + r]) // k)
+    return np.array(sorted(tok))
 
 
 def test_fused_mixtral_m32(dev):
@@ -280,7 +348,7 @@ def test_fused_fp8_full_sizes(dev, M):
     oracle needs comes from tests/golden/fp8_act_amax.json (written by the
     oracle), after checking that the seeded inputs are the ones it used."""
     import json
-    say(f"fused fp8_e4m3 M={M} (sampled tokens, golden amax)")
+    say(f"fused fp8_e4m3 M={M} (golden amax)")
     gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fp8_act_amax.json")))
     cfg = CONFIGS["fp8_e4m3"]
     w, _ = weights(cfg, dev)
@@ -293,7 +361,10 @@ def test_fused_fp8_full_sizes(dev, M):
     # weight draws on the GPU may differ from the CPU draw in a last bit of a value
     np.testing.assert_allclose([float(v) for v in w["w1_scale"][:8]], fp["w1_scale"], rtol=1e-6)
     np.testing.assert_allclose([float(v) for v in w["w2_scale"][:8]], fp["w2_scale"], rtol=1e-6)
-    check_layer(cfg, M, dev, tokens=[t for t in SAMPLE + [M - 1] if t < M], act_amax=gold["amax"][str(M)], batch=b)
+    # 32 tokens: all of them; 512 tokens: every 128-row tile of the grid (rows
+    # in both wavefront halves and the last real row of each tile)
+    tok = None if M <= 32 else tile_tokens(b["logits"].cpu(), cfg.E, cfg.topk, 128, rows=(0, 70))
+    check_layer(cfg, M, dev, tokens=tok, act_amax=gold["amax"][str(M)], batch=b)
 
 
 def test_paths_agree_eq2_identity(dev, monkeypatch):
@@ -337,8 +408,44 @@ def test_fused_edge_shapes(dev, dtype, E, k, H, I, M):
 
 
 def test_fused_layer_full_prefill(dev):
-    say("fused mixtral_prefill_bf16 M=4096 (sampled tokens)")
-    check_layer(CONFIGS["mixtral_prefill_bf16"], 4096, dev, tokens=[0, 1, 2, 1000, 2047, 3000, 4094, 4095])
+    """The 4096-token prefill layer: compared tokens chosen so that every
+    128-row tile of the Zipf-skewed grid holds compared pairs."""
+    cfg = CONFIGS["mixtral_prefill_bf16"]
+    b = layer_batch(cfg, 4096, dev)
+    tok = tile_tokens(b["logits"].cpu(), cfg.E, cfg.topk, 128)
+    say(f"fused mixtral_prefill_bf16 M=4096 ({len(tok)} tokens covering every row tile)")
+    check_layer(cfg, 4096, dev, tokens=tok, batch=b)
+
+
+def test_fused_prefill_deterministic(dev):
+    cfg = replace(CONFIGS["mixtral_prefill_bf16"], H=1024, I=1024)
+    say("determinism (tile kernels)")
+    w, _ = weights(cfg, dev)
+    b = layer_batch(cfg, 600, dev)
+    o1 = run_fused(cfg, b, w, dev).clone()
+    o2 = run_fused(cfg, b, w, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_fp8_scale_product_invariance_gpu(dev, M):
+    """(2 s_x, s_w1 / 2) leaves every product scale, hence the intermediate,
+    its amax and the output, bit for bit unchanged; scaling s_w2 by 4 scales
+    the output by 4 exactly (bf16 rounding commutes with powers of two)."""
+    cfg = replace(CONFIGS["fp8_e4m3"], E=16, H=512, I=512)
+    say(f"fp8 scale-product invariance M={M}")
+    w, _ = weights(cfg, dev)
+    b = layer_batch(cfg, M, dev)
+    o1 = run_fused(cfg, b, w, dev).clone()
+    b2 = dict(b, x_scale=b["x_scale"] * 2)
+    w2 = dict(w, w1_scale=w["w1_scale"] / 2)
+    o2 = run_fused(cfg, b2, w2, dev).clone()
+    w4 = dict(w, w2_scale=w["w2_scale"] * 4)
+    o4 = run_fused(cfg, b, w4, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(o4.float(), o1.float() * 4)
 
 
 def test_fused_deterministic(dev):
