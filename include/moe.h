@@ -41,7 +41,8 @@ typedef enum {
     MOE_ERR_UNSUPPORTED = 3, /* E>256, topk>16, dtype/kind combination, block_m      */
     MOE_ERR_WORKSPACE = 4,   /* workspace smaller than fused_moe_workspace_size()   */
     MOE_ERR_ALIGNMENT = 5,   /* a pointer is not 16-byte aligned                    */
-    MOE_ERR_HIP = 6          /* a HIP launch failed                                 */
+    MOE_ERR_HIP = 6,         /* a HIP launch failed                                 */
+    MOE_ERR_SCRATCH = 7      /* fused_moe_noalloc: sizes need more than its scratch */
 } moe_status;
 
 typedef enum {
@@ -176,6 +177,34 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
                      int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize,
                      void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* Bytes of the static device scratch behind fused_moe_noalloc (64 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* fused_moe without a workspace argument, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments,
+ * results and errors as fused_moe, except that the workspace is a
+ * file-scope device array of MOE_NOALLOC_SCRATCH_BYTES inside the library:
+ *  - each GPU the library runs on holds its own copy until the process
+ *    ends; its address is looked up (hipGetSymbolAddress) on the first call
+ *    on each device and kept, so that call is not capturable;
+ *  - sizes whose workspace (fused_moe_workspace_size) exceeds
+ *    MOE_NOALLOC_SCRATCH_BYTES are rejected with MOE_ERR_SCRATCH before any
+ *    HIP call (64 MiB covers the decode batches up to 64 tokens of every
+ *    layer shape here);
+ *  - the call allocates nothing and frees nothing;
+ *  - every call on one GPU uses the same scratch, whose contents on entry do
+ *    not matter: calls that overlap in time on one GPU (different streams,
+ *    or different host threads without ordering) race and give undefined
+ *    results. */
+moe_status fused_moe_noalloc(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
+                             const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
+                             int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize,
+                             void* out, int32_t* topk_ids_out, float* topk_weights_out, void* stream);
+
+/* MOE_NOALLOC_SCRATCH_BYTES, as a call (for bindings that cannot read macros). */
+size_t fused_moe_noalloc_scratch_bytes(void);
 
 /* Static description of a status code. */
 const char* moe_status_str(moe_status s);

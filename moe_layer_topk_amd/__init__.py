@@ -18,6 +18,7 @@ import ctypes
 import torch
 
 from ._lib import (  # noqa: F401
+    MOE_ERR_SCRATCH,
     MOE_BF16,
     MOE_F32,
     MOE_FP8_E4M3,
@@ -152,4 +153,20 @@ def fused_moe(x, router_logits, w1, w2, topk: int, renormalize: bool = True, x_s
     check(lib().fused_moe(dt, _p(x), _p(x_scale), _p(router_logits), _p(w1), _p(w1_scale), _p(w2), _p(w2_scale),
                           M, E, topk, H, I, int(renormalize), _p(out), _p(topk_ids), _p(topk_weights),
                           _p(workspace), workspace.numel(), _stream(x)), "fused_moe")
+    return out
+
+
+def fused_moe_noalloc(x, router_logits, w1, w2, topk: int, renormalize: bool = True, x_scale=None, w1_scale=None,
+                      w2_scale=None, out=None, topk_ids=None, topk_weights=None):
+    """fused_moe with the library's static device scratch as its workspace
+    (no workspace argument; calls overlapping on one GPU race)."""
+    M, H = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    dt = moe_dtype(w1)
+    if out is None:
+        out = torch.empty((M, H), dtype=_INTER[dt], device=x.device)
+    check(lib().fused_moe_noalloc(dt, _p(x), _p(x_scale), _p(router_logits), _p(w1), _p(w1_scale), _p(w2),
+                                  _p(w2_scale), M, E, topk, H, I, int(renormalize), _p(out), _p(topk_ids),
+                                  _p(topk_weights), _stream(x)), "fused_moe_noalloc")
     return out

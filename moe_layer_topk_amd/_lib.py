@@ -7,7 +7,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_ALIGNMENT, MOE_ERR_HIP = range(7)
+(MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_ALIGNMENT, MOE_ERR_HIP,
+ MOE_ERR_SCRATCH) = range(8)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_GEMM_GATE_UP_SILU, MOE_GEMM_DOWN, MOE_GEMM_DOWN_E4M3_ACT = 0, 1, 2
 
@@ -38,6 +39,9 @@ SIGNATURES = {
     "fused_moe_workspace_size": (_SZ, [ctypes.c_int, _I32, _I32, _I32, _I32, _I32]),
     "fused_moe": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _P, _P, _P, _P, _SZ, _P]),
+    "fused_moe_noalloc": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                         _I32, _P, _P, _P, _P]),
+    "fused_moe_noalloc_scratch_bytes": (_SZ, []),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_launch.h"
 
 using namespace moe;
@@ -111,6 +113,7 @@ const char* moe_status_str(moe_status s) {
         case MOE_ERR_WORKSPACE: return "workspace too small";
         case MOE_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
         case MOE_ERR_HIP: return "HIP launch failed";
+        case MOE_ERR_SCRATCH: return "sizes exceed the static scratch of fused_moe_noalloc";
     }
     return "unknown status";
 }
@@ -211,11 +214,15 @@ size_t fused_moe_workspace_size(moe_dtype dtype, int32_t M, int32_t E, int32_t t
     return fused_layout(nullptr, dtype, M, E, topk, H, I).bytes;
 }
 
-moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
-                     const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
-                     int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize,
-                     void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by fused_moe and fused_moe_noalloc (host only).
+moe_status check_fused(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
+                       const void* w1, const float* w1_scale, const void* w2, const float* w2_scale, int32_t M,
+                       int32_t E, int32_t topk, int32_t H, int32_t I, const void* out, const int32_t* topk_ids_out,
+                       const float* topk_weights_out) {
     if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
     moe_status st = check_router(M, E, topk);
     if (st != MOE_OK) return st;
@@ -224,16 +231,20 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
     if (fp8 && (H % 256 || I % 256)) return MOE_ERR_SHAPE;
     if (!fp8 && (x_scale || w1_scale || w2_scale)) return MOE_ERR_UNSUPPORTED;
     if (M == 0) return MOE_OK;
-    if (!x || !router_logits || !w1 || !w2 || !out || !workspace) return MOE_ERR_NULL;
+    if (!x || !router_logits || !w1 || !w2 || !out) return MOE_ERR_NULL;
     if (fp8 && (!x_scale || !w1_scale || !w2_scale)) return MOE_ERR_NULL;
     if (misaligned(x) || misaligned(router_logits) || misaligned(w1) || misaligned(w2) || misaligned(out) ||
         misaligned(topk_ids_out) || misaligned(topk_weights_out))
         return MOE_ERR_ALIGNMENT;
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_ERR_ALIGNMENT;
-    FusedLayout L = fused_layout(static_cast<char*>(workspace), dtype, M, E, topk, H, I);
-    if (workspace_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
+// The launch sequence over a carved workspace (arguments already checked, M > 0).
+moe_status run_fused(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
+                     const void* w1, const float* w1_scale, const void* w2, const float* w2_scale, int32_t M,
+                     int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize, void* out,
+                     int32_t* topk_ids_out, float* topk_weights_out, const FusedLayout& L, hipStream_t s) {
+    const bool fp8 = dtype == MOE_FP8_E4M3;
     int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;
     float* wts = topk_weights_out ? topk_weights_out : L.wts;
     if (route_align_fits(M)) {
@@ -258,6 +269,79 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
     if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
     if (L.ksplit > 1) return hip_status(launch_combine_partials(L.ypart, L.ksplit, wts, M, topk, H, inter, out, s));
     return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));
+}
+
+// ------------------------------------------------------ static scratch
+//
+// The workspace of fused_moe_noalloc: a file-scope device array, one copy
+// per GPU for the life of the process.  Host code never uses the array's
+// name as an address (on the host it only names the symbol); its device
+// address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and kept.
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
+// The current device's scratch address, or nullptr (with *err set) if the
+// lookup fails.
+void* scratch_for_current_device(hipError_t* err) {
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        scratch_dev[dev] = p;
+    }
+    return scratch_dev[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
+                     const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
+                     int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize,
+                     void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    moe_status st = check_fused(dtype, x, x_scale, router_logits, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, out,
+                                topk_ids_out, topk_weights_out);
+    if (st != MOE_OK || M == 0) return st;
+    if (!workspace) return MOE_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_ERR_ALIGNMENT;
+    FusedLayout L = fused_layout(static_cast<char*>(workspace), dtype, M, E, topk, H, I);
+    if (workspace_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+    return run_fused(dtype, x, x_scale, router_logits, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, renormalize, out,
+                     topk_ids_out, topk_weights_out, L, static_cast<hipStream_t>(stream));
+}
+
+size_t fused_moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+moe_status fused_moe_noalloc(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
+                             const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
+                             int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize,
+                             void* out, int32_t* topk_ids_out, float* topk_weights_out, void* stream) {
+    moe_status st = check_fused(dtype, x, x_scale, router_logits, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, out,
+                                topk_ids_out, topk_weights_out);
+    if (st != MOE_OK || M == 0) return st;
+    // sizes first (host only), then the one-time address lookup
+    if (fused_layout(nullptr, dtype, M, E, topk, H, I).bytes > kScratchBytes) return MOE_ERR_SCRATCH;
+    hipError_t err = hipSuccess;
+    void* ws = scratch_for_current_device(&err);
+    if (!ws) return MOE_ERR_HIP;
+    FusedLayout L = fused_layout(static_cast<char*>(ws), dtype, M, E, topk, H, I);
+    return run_fused(dtype, x, x_scale, router_logits, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, renormalize, out,
+                     topk_ids_out, topk_weights_out, L, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert L.moe_status_str(s)
     assert L.moe_status_str(0) == b"ok"
 
@@ -161,3 +161,25 @@ def test_bench_refuses_several_gpus():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_fused_noalloc_validation(L):
+    """fused_moe_noalloc checks its arguments like fused_moe and rejects sizes
+    beyond its static scratch before any HIP call."""
+    from moe_layer_topk_amd._lib import MOE_ERR_SCRATCH
+    assert L.fused_moe_noalloc_scratch_bytes() == 64 << 20
+    args = lambda dt, M, E, k, H, I: (dt, FAKE, None, FAKE, FAKE, None, FAKE, None, M, E, k, H, I, 1, FAKE, None,  # noqa
+                                      None, NULL)
+    # the 4096-token Mixtral-shaped bf16 layer needs ~280 MB of workspace
+    assert L.fused_moe_workspace_size(1, 4096, 8, 2, 4096, 14336) > (64 << 20)
+    assert L.fused_moe_noalloc(*args(1, 4096, 8, 2, 4096, 14336)) == MOE_ERR_SCRATCH
+    assert L.fused_moe_noalloc(*args(1, 4, 8, 9, 256, 256)) == 2
+    assert L.fused_moe_noalloc(*args(5, 4, 8, 2, 256, 256)) == 3
+    assert L.fused_moe_noalloc(1, NULL, None, FAKE, FAKE, None, FAKE, None, 4, 8, 2, 256, 256, 1, FAKE, None, None,
+                               NULL) == 1
+    assert L.fused_moe_noalloc(1, ODD, None, FAKE, FAKE, None, FAKE, None, 4, 8, 2, 256, 256, 1, FAKE, None, None,
+                               NULL) == 5
+    assert L.fused_moe_noalloc(*args(1, 0, 8, 2, 256, 256)) == 0  # M = 0: no-op
+    # every decode batch (up to 64 tokens) of every layer shape fits
+    for dt, E, k, H, I in [(1, 8, 2, 4096, 14336), (1, 128, 8, 2048, 768), (2, 64, 8, 4096, 8192)]:
+        assert L.fused_moe_workspace_size(dt, 64, E, k, H, I) <= (64 << 20)
