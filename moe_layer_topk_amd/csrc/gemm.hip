@@ -24,6 +24,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -639,14 +641,15 @@ constexpr int kP2Xcds = 8;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // 16 bytes per lane from global memory straight into LDS: the wave's 64
-// lanes fill 1 KB at the wave-uniform LDS address in M0.  Issued through
-// inline asm so the compiler does not treat every later LDS read as
+// lanes fill 1 KB at the wave-uniform LDS byte address in M0 (a 32-bit LDS
+// address, so a ring's stage addresses are plain scalar adds).  Issued
+// through inline asm so the compiler does not treat every later LDS read as
 // dependent on the copy (it would wait for all copies in flight, prefetched
-// stages included); the kernel orders the ring itself with explicit vmcnt
-// waits and barriers.  "memory" keeps LDS reads and writes of the kernel in
-// program order around it.
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
-    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)lds_dst);
+// stages included); the kernels order their rings themselves with explicit
+// vmcnt waits and barriers.  "memory" keeps LDS reads and writes of the
+// kernel in program order around it.
+__device__ __forceinline__ void lds_dma16_at(const void* src, unsigned lds_addr) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
 
@@ -654,9 +657,13 @@ __device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
 // weights), so the stream does not displace reused lines (token rows) from
 // L2; on MI355X it also streams faster (weights of the Mixtral-shaped gate/up
 // projection through the decode ring: 5.83 TB/s plain, 6.59 TB/s with nt).
-__device__ __forceinline__ void lds_dma16_nt(const void* src, char* lds_dst) {
-    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)lds_dst);
+__device__ __forceinline__ void lds_dma16_nt_at(const void* src, unsigned lds_addr) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr_of(const void* p) {
+    return (unsigned)(uintptr_t)(const lds_void*)p;
 }
 
 // wait until at most n vector-memory operations of this wave are outstanding
@@ -787,20 +794,21 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
     }
 
     // copy instructions [j0, j1) of stage kt (A rows first, then B rows)
+    const unsigned lds0 = lds_addr_of(p2_lds);
     auto issue_part = [&](int kt, int j0, int j1) {
-        char* st = p2_lds + (kt % C::ST) * C::StageBytes;
+        const unsigned st = lds0 + (unsigned)((kt % C::ST) * C::StageBytes);
         const size_t koff = (size_t)kt * C::RowBytes;
 #pragma unroll
         for (int j = 0; j < C::L; ++j) {
             if (j < j0 || j >= j1) continue;
             if (j < C::ALoads)
-                lds_dma16(asrc[j] + koff, st + (wave * C::ALoads + j) * C::RowsPerLoad * C::RowBytes);
+                lds_dma16_at(asrc[j] + koff, st + (wave * C::ALoads + j) * C::RowsPerLoad * C::RowBytes);
             else if constexpr (NTW)
-                lds_dma16_nt(bsrc[j - C::ALoads] + koff,
-                             st + C::ABytes + (wave * C::BLoads + (j - C::ALoads)) * C::RowsPerLoad * C::RowBytes);
+                lds_dma16_nt_at(bsrc[j - C::ALoads] + koff,
+                                st + C::ABytes + (wave * C::BLoads + (j - C::ALoads)) * C::RowsPerLoad * C::RowBytes);
             else
-                lds_dma16(bsrc[j - C::ALoads] + koff,
-                          st + C::ABytes + (wave * C::BLoads + (j - C::ALoads)) * C::RowsPerLoad * C::RowBytes);
+                lds_dma16_at(bsrc[j - C::ALoads] + koff,
+                             st + C::ABytes + (wave * C::BLoads + (j - C::ALoads)) * C::RowsPerLoad * C::RowBytes);
         }
     };
     auto issue = [&](int kt) { issue_part(kt, 0, C::L); };
@@ -838,15 +846,21 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
 #pragma unroll
     for (int s0 = 0; s0 < C::ST - 1; ++s0)
         if (s0 < nk) issue(s0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int ahead = min(C::ST - 2, nk - 1 - kt);  // later stages already issued
-        wait_vm_runtime<C::L>(ahead);
+    // one stage; PF: the copies of stage kt + ST - 1 are issued during it (every
+    // stage but the last ST - 1, which run as a separate tail so that the main
+    // loop carries no per-copy condition)
+    auto stage = [&](int kt, auto pf_tag) {
+        constexpr bool pf = decltype(pf_tag)::value;
+        if constexpr (pf) {
+            wait_vm<(C::ST - 2) * C::L < 64 ? (C::ST - 2) * C::L : 63>();  // stage kt landed; ST - 2 later ones in flight
+        } else {
+            wait_vm_runtime<C::L>(min(C::ST - 2, nk - 1 - kt));
+        }
         __syncthreads();
         // the copies of stage kt + ST - 1 (into the buffer every wave finished
         // reading before this barrier) are spread over the K substeps, between
         // MFMA groups, so the wave never stalls on a burst of copies while its
         // matrix core idles
-        const bool pf = kt + C::ST - 1 < nk;
         const char* st = p2_lds + (kt % C::ST) * C::StageBytes;
         const char* sa = st;
         const char* sb = st + C::ABytes;
@@ -898,7 +912,10 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    const int nmain = nk - (C::ST - 1) > 0 ? nk - (C::ST - 1) : 0;
+    for (int kt = 0; kt < nmain; ++kt) stage(kt, std::true_type{});
+    for (int kt = nmain; kt < nk; ++kt) stage(kt, std::false_type{});
 
     // ---- epilogue: lane holds C[8*(v/4) + 4*(lane/32) + v%4][lane%32] of each 32x32 tile
     float amax = 0.0f;
@@ -1086,6 +1103,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
     const ActQuant quant(qs);
 
     char* ring = ring_lds + wave * (KD * R::Stage);
+    const unsigned ring_lds0 = lds_addr_of(ring);
     f32x4* red = reinterpret_cast<f32x4*>(ring_lds);  // after the main loop only
     float amax = 0.0f;
 
@@ -1114,18 +1132,19 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
         auto issue = [&](int j) {
             const int s = wave + 4 * j;
             const int gi = s / nks, ks = ks0 + s % nks;
-            char* st = ring + (j % KD) * R::Stage;
+            const unsigned st = ring_lds0 + (unsigned)((j % KD) * R::Stage);
             // this wave's earlier LDS reads of the slot have completed
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             const char* wsrc = wexp + gi * gstride + (size_t)ks * kRingSB;
 #pragma unroll
-            for (int i = 0; i < R::WInstr; ++i) lds_dma16_nt(wsrc + woff[i], st + i * 1024);
+            for (int i = 0; i < R::WInstr; ++i) lds_dma16_nt_at(wsrc + woff[i], st + i * 1024);
             if constexpr (!TQ) {
                 const char* tsrc = reinterpret_cast<const char*>(g.a) + (size_t)ks * kRingSB;
 #pragma unroll
                 for (int c = 0; c < NT; ++c)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) lds_dma16(tsrc + toff[c][h], st + R::TokOff + (2 * c + h) * 1024);
+                    for (int h = 0; h < 2; ++h)
+                        lds_dma16_at(tsrc + toff[c][h], st + R::TokOff + (2 * c + h) * 1024);
             }
         };
         // TQ: the float32 operand values of step j (elements 16 lg.. and 64 + 16 lg.. of the
