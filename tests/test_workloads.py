@@ -64,3 +64,19 @@ def test_tiny_router_logits_are_x_wg():
     b = layer_batch(cfg, 16, "cpu")
     assert b["logits"].shape == (16, 8) and b["x"].dtype == torch.float32
     assert torch.equal(layer_batch(cfg, 16, "cpu")["logits"], b["logits"])
+
+
+def test_whole_tensor_weights_equal_per_expert_draws():
+    """layer_weights draws all experts in one fill; expert e must hold the same
+    bytes as its own draw at offset e * (elements per expert matrix)."""
+    from dataclasses import replace
+    from workloads.gen import S_W1, S_W2, normal_bf16, normal_f32
+    for name, mk in (("finegrained_bf16", normal_bf16), ("tiny_f32", normal_f32)):
+        cfg = replace(CONFIGS[name], E=5, H=128, I=256)
+        w = layer_weights(cfg, "cpu")
+        sub = layer_weights(cfg, "cpu", experts=[1, 4])
+        n1, n2 = 2 * cfg.I * cfg.H, cfg.H * cfg.I
+        for e in range(cfg.E):
+            assert torch.equal(w["w1"][e], mk(0, S_W1, (2 * cfg.I, cfg.H), cfg.weight_std, "cpu", offset=e * n1))
+            assert torch.equal(w["w2"][e], mk(0, S_W2, (cfg.H, cfg.I), cfg.weight_std, "cpu", offset=e * n2))
+        assert torch.equal(sub["w1"][4], w["w1"][4]) and not sub["w1"][0].any()

@@ -113,6 +113,22 @@ def normal_bf16(seed, stream, shape, std, device, offset=0) -> torch.Tensor:
     return normal_f32(seed, stream, shape, std, device, offset).to(torch.bfloat16)
 
 
+def fill_normal(dst: torch.Tensor, seed: int, stream: int, std: float, offset: int = 0) -> torch.Tensor:
+    """normal_f32 / normal_bf16 of dst's shape written into dst (float32 or
+    bfloat16, contiguous) chunk by chunk: the same bytes, with a few large
+    launches and no whole-tensor float64 temporary."""
+    flat = dst.view(-1)
+    n = flat.numel()
+    chunk = _CHUNK_CPU if dst.device.type == "cpu" else _CHUNK_GPU
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        z = counter_normal(seed, stream, e - s, dst.device, offset + s)
+        if std != 1.0:
+            z = z * std
+        flat[s:e] = z.to(torch.float32).to(dst.dtype)
+    return dst
+
+
 def _quant_e4m3_per_tensor(v: torch.Tensor):
     """Store a float32 tensor as OCP e4m3 with one float32 scale s = amax/448.
 
@@ -186,6 +202,11 @@ def layer_weights(cfg: LayerConfig, device, seed: int = 0, experts=None) -> dict
         return {"w1": w1, "w2": w2, "w1_scale": s1, "w2_scale": s2}
     mk = normal_bf16 if cfg.dtype == "bf16" else normal_f32
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    if experts is None:
+        # expert e's element i is element e * n + i of one stream: all experts in one fill
+        w1 = fill_normal(torch.empty((E, 2 * I, H), dtype=dt, device=device), seed, S_W1, cfg.weight_std)
+        w2 = fill_normal(torch.empty((E, H, I), dtype=dt, device=device), seed, S_W2, cfg.weight_std)
+        return {"w1": w1, "w2": w2, "w1_scale": None, "w2_scale": None}
     w1 = torch.zeros((E, 2 * I, H), dtype=dt, device=device)
     w2 = torch.zeros((E, H, I), dtype=dt, device=device)
     for e in sel:
