@@ -78,6 +78,23 @@ typedef struct {
     int32_t* num_active;
 } moe_align_bufs;
 
+/* Router scores (FusedMoE vs MegaMoE post, section 2: the router yields a
+ * score per expert for every token, from which the weight distribution and
+ * the top-k are taken):
+ *  logits[t][e] = sum_h x[t][h] * router_w[e][h], float32 accumulation.
+ *  x         device [M][H] in x_dtype: MOE_F32, MOE_BF16, or MOE_FP8_E4M3 with
+ *            x_scale -> its float32 per-tensor scale (x_scale must be NULL
+ *            otherwise)
+ *  router_w  device float32 [E][H] (K-contiguous, like the expert weights)
+ *  logits    device float32 [M][E]
+ * Every score is computed the same way (lane l of a wavefront sums, in
+ * ascending h, the products at h = 256 i + 4 l + j, j = 0..3, and the 64
+ * partials are combined by a butterfly), so the result does not depend on
+ * the batch or on which entry point computes it.  H must be a multiple of 4.  Errors: NULL ->
+ * MOE_ERR_NULL; M<0, H<1, E<1 -> MOE_ERR_SHAPE; bad dtype -> MOE_ERR_UNSUPPORTED. */
+moe_status moe_router_logits(moe_dtype x_dtype, const void* x, const float* x_scale, const float* router_w,
+                             int32_t M, int32_t H, int32_t E, float* logits, void* stream);
+
 /* Top-k routing (FusedMoE vs MegaMoE post, section 2; section 3.1 step 1).
  *  logits        device, float32 [M][E], finite (non-finite values give
  *                unspecified ids, but every id written is in [0, E))
@@ -177,6 +194,22 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
                      int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize,
                      void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* fused_moe from the hidden states: the router scores are computed on the
+ * GPU first (router_w device float32 [E][H]; router_logits is then an OUTPUT,
+ * device float32 [M][E], that receives them), and the layer routes on those
+ * scores (the MoE kernel engineering post's introduction: routing, data
+ * shuffling and expert compute as one batched GPU operation).  For a few
+ * tokens and a small router (up to 16 tokens, 64 K router weights and 128 K
+ * multiply-adds) scoring, top-k and alignment are one launch; otherwise
+ * moe_router_logits runs first.  The scores are the same bits either way.
+ * Workspace, arguments and errors as for fused_moe (fused_moe_workspace_size
+ * gives the workspace). */
+moe_status fused_moe_router(moe_dtype dtype, const void* x, const float* x_scale, const float* router_w,
+                            float* router_logits, const void* w1, const float* w1_scale, const void* w2,
+                            const float* w2_scale, int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I,
+                            int32_t renormalize, void* out, int32_t* topk_ids_out, float* topk_weights_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of the static device scratch behind fused_moe_noalloc (64 MiB). */
 #define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)

@@ -170,3 +170,37 @@ def fused_moe_noalloc(x, router_logits, w1, w2, topk: int, renormalize: bool = T
                                   _p(w2_scale), M, E, topk, H, I, int(renormalize), _p(out), _p(topk_ids),
                                   _p(topk_weights), _stream(x)), "fused_moe_noalloc")
     return out
+
+
+def moe_router_logits(x, router_w, x_scale=None, out=None):
+    """Router scores float32 [M, E] = x . router_w^T (router_w float32 [E, H])."""
+    M, H = x.shape
+    E = router_w.shape[0]
+    if router_w.dtype != torch.float32:
+        raise ValueError("router weights are float32")
+    lg = out if out is not None else torch.empty((M, E), dtype=torch.float32, device=x.device)
+    check(lib().moe_router_logits(moe_dtype(x), _p(x), _p(x_scale), _p(router_w), M, H, E, _p(lg), _stream(x)),
+          "moe_router_logits")
+    return lg
+
+
+def fused_moe_router(x, router_w, w1, w2, topk: int, renormalize: bool = True, x_scale=None, w1_scale=None,
+                     w2_scale=None, workspace=None, out=None, logits=None, topk_ids=None, topk_weights=None):
+    """The whole layer from the hidden states: router scores on the GPU (written
+    to `logits`, float32 [M, E]), then route -> align -> experts -> combine.
+    Returns (out, logits)."""
+    M, H = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    dt = moe_dtype(w1)
+    need = fused_moe_workspace_size(dt, M, E, topk, H, I)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, H), dtype=_INTER[dt], device=x.device)
+    if logits is None:
+        logits = torch.empty((M, E), dtype=torch.float32, device=x.device)
+    check(lib().fused_moe_router(dt, _p(x), _p(x_scale), _p(router_w), _p(logits), _p(w1), _p(w1_scale), _p(w2),
+                                 _p(w2_scale), M, E, topk, H, I, int(renormalize), _p(out), _p(topk_ids),
+                                 _p(topk_weights), _p(workspace), workspace.numel(), _stream(x)), "fused_moe_router")
+    return out, logits

@@ -39,6 +39,9 @@ SIGNATURES = {
     "fused_moe_workspace_size": (_SZ, [ctypes.c_int, _I32, _I32, _I32, _I32, _I32]),
     "fused_moe": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _P, _P, _P, _P, _SZ, _P]),
+    "moe_router_logits": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _I32, _I32, _I32, _P, _P]),
+    "fused_moe_router": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                        _I32, _P, _P, _P, _P, _SZ, _P]),
     "fused_moe_noalloc": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                          _I32, _P, _P, _P, _P]),
     "fused_moe_noalloc_scratch_bytes": (_SZ, []),

@@ -240,21 +240,34 @@ moe_status check_fused(moe_dtype dtype, const void* x, const float* x_scale, con
 }
 
 // The launch sequence over a carved workspace (arguments already checked, M > 0).
+// router_w non-null: router_logits is an output the layer first fills with
+// x . router_w^T (in the same launch as route + align when that fits).
 moe_status run_fused(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
                      const void* w1, const float* w1_scale, const void* w2, const float* w2_scale, int32_t M,
                      int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize, void* out,
-                     int32_t* topk_ids_out, float* topk_weights_out, const FusedLayout& L, hipStream_t s) {
+                     int32_t* topk_ids_out, float* topk_weights_out, const FusedLayout& L, hipStream_t s,
+                     const float* router_w = nullptr) {
     const bool fp8 = dtype == MOE_FP8_E4M3;
     int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;
     float* wts = topk_weights_out ? topk_weights_out : L.wts;
-    if (route_align_fits(M)) {
-        if (launch_route_align(router_logits, M, E, topk, renormalize, ids, wts, L.block_m, L.cap, L.al,
-                               fp8 ? L.amax : nullptr, s) != hipSuccess)
+    float* logits = const_cast<float*>(router_logits);
+    if (router_w && router_route_align_fits(M, E, H)) {
+        // router scores, top-k and alignment in one launch
+        if (launch_router_route_align(dtype, x, x_scale, router_w, H, logits, M, E, topk, renormalize, ids, wts,
+                                      L.block_m, L.cap, L.al, fp8 ? L.amax : nullptr, s) != hipSuccess)
             return MOE_ERR_HIP;
     } else {
-        if (launch_route(router_logits, M, E, topk, renormalize, ids, wts, s) != hipSuccess) return MOE_ERR_HIP;
-        if (launch_align(ids, M, topk, E, L.block_m, L.cap, L.al, fp8 ? L.amax : nullptr, s) != hipSuccess)
+        if (router_w && launch_router_logits(dtype, x, x_scale, router_w, M, E, H, logits, s) != hipSuccess)
             return MOE_ERR_HIP;
+        if (route_align_fits(M)) {
+            if (launch_route_align(logits, M, E, topk, renormalize, ids, wts, L.block_m, L.cap, L.al,
+                                   fp8 ? L.amax : nullptr, s) != hipSuccess)
+                return MOE_ERR_HIP;
+        } else {
+            if (launch_route(logits, M, E, topk, renormalize, ids, wts, s) != hipSuccess) return MOE_ERR_HIP;
+            if (launch_align(ids, M, topk, E, L.block_m, L.cap, L.al, fp8 ? L.amax : nullptr, s) != hipSuccess)
+                return MOE_ERR_HIP;
+        }
     }
     const moe_dtype inter = dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
     GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, x, x_scale, w1, w1_scale, L.al, M, topk, E, 2 * I, H,
@@ -323,6 +336,35 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
     if (workspace_bytes < L.bytes) return MOE_ERR_WORKSPACE;
     return run_fused(dtype, x, x_scale, router_logits, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, renormalize, out,
                      topk_ids_out, topk_weights_out, L, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_router_logits(moe_dtype x_dtype, const void* x, const float* x_scale, const float* router_w,
+                             int32_t M, int32_t H, int32_t E, float* logits, void* stream) {
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16 && x_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if (M < 0 || H < 1 || E < 1 || H % 4) return MOE_ERR_SHAPE;
+    if ((x_dtype == MOE_FP8_E4M3) != (x_scale != nullptr)) return x_scale ? MOE_ERR_UNSUPPORTED : MOE_ERR_NULL;
+    if (M == 0) return MOE_OK;
+    if (!x || !router_w || !logits) return MOE_ERR_NULL;
+    if (misaligned(x) || misaligned(router_w) || misaligned(logits)) return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_router_logits(x_dtype, x, x_scale, router_w, M, E, H, logits,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status fused_moe_router(moe_dtype dtype, const void* x, const float* x_scale, const float* router_w,
+                            float* router_logits, const void* w1, const float* w1_scale, const void* w2,
+                            const float* w2_scale, int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I,
+                            int32_t renormalize, void* out, int32_t* topk_ids_out, float* topk_weights_out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    moe_status st = check_fused(dtype, x, x_scale, router_logits, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, out,
+                                topk_ids_out, topk_weights_out);
+    if (st != MOE_OK || M == 0) return st;
+    if (!router_w || !workspace) return MOE_ERR_NULL;
+    if (misaligned(router_w)) return MOE_ERR_ALIGNMENT;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_ERR_ALIGNMENT;
+    FusedLayout L = fused_layout(static_cast<char*>(workspace), dtype, M, E, topk, H, I);
+    if (workspace_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+    return run_fused(dtype, x, x_scale, router_logits, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, renormalize, out,
+                     topk_ids_out, topk_weights_out, L, static_cast<hipStream_t>(stream), router_w);
 }
 
 size_t fused_moe_noalloc_scratch_bytes(void) { return kScratchBytes; }

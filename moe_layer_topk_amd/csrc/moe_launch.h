@@ -29,6 +29,17 @@ hipError_t launch_route_align(const float* logits, int M, int E, int topk, int r
                               float* weights, int block_m, int64_t cap, const moe_align_bufs& out,
                               float* zero_f32, hipStream_t s);
 
+// Router scores logits[M][E] = x . wg^T (wg float32 [E][H]).
+hipError_t launch_router_logits(moe_dtype xdt, const void* x, const float* x_scale, const float* wg, int M, int E,
+                                int H, float* logits, hipStream_t s);
+
+// Router + route + align in one launch, for a few tokens and a small router.
+bool router_route_align_fits(int M, int E, int H);
+hipError_t launch_router_route_align(moe_dtype xdt, const void* x, const float* x_scale, const float* wg, int H,
+                                     float* logits_out, int M, int E, int topk, int renormalize, int32_t* ids,
+                                     float* weights, int block_m, int64_t cap, const moe_align_bufs& out,
+                                     float* zero_f32, hipStream_t s);
+
 hipError_t launch_fill_zero_f32(float* p, int n, hipStream_t s);
 
 struct GemmCall {

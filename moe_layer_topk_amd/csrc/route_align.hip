@@ -117,6 +117,160 @@ hipError_t launch_route(const float* logits, int M, int E, int topk, int renorma
     return hipGetLastError();
 }
 
+constexpr int kAlignWavesR = 16;      // wavefronts of the one-workgroup route + align launch
+constexpr int kRouteRouterMaxM = 16;  // tokens it scores with the router itself
+
+// ----------------------------------------------------------------- router
+//
+// logits[t][e] = sum_h x[t][h] * wg[e][h] (FusedMoE vs MegaMoE post,
+// section 2: the router scores every expert for every token), wg float32
+// [E][H], x float32, bfloat16 or e4m3 times its per-tensor scale.
+
+// Four consecutive activations x[i..i+3] as float32 (e4m3: their values
+// times the scale); i is a multiple of 4 and rows are 16-byte aligned.
+template <int XDT>
+__device__ __forceinline__ float4 router_x4(const void* x, size_t i, float sx) {
+    if constexpr (XDT == MOE_F32) {
+        return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + i);
+    } else if constexpr (XDT == MOE_BF16) {
+        const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + i);
+        return float4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                      __uint_as_float(v.y & 0xffff0000u)};
+    } else {
+        // OCP e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits, no inf
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(x) + i);
+        float r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t c = (w >> (8 * j)) & 0xffu, ef = (c >> 3) & 15, m = c & 7;
+            float v;
+            if (ef == 15 && m == 7) v = __uint_as_float(0x7fc00000u);
+            else if (ef == 0) v = (float)m * (1.0f / 512.0f);
+            else v = __uint_as_float(((ef + 120u) << 23) | (m << 20));
+            r[j] = ((c & 0x80u) ? -v : v) * sx;
+        }
+        return float4{r[0], r[1], r[2], r[3]};
+    }
+}
+
+// The scores of a block of TT tokens x TE experts by one wavefront.  Every
+// score is defined the same way wherever it is computed: lane l sums, in
+// ascending h, the products at h = 256 i + 4 l + j (j = 0..3), and the 64
+// lane partials are combined by a butterfly (offsets 32, 16, ..., 1; every
+// lane ends with the same sum).  So the one-workgroup front end and the
+// many-token kernel give the same bits.
+template <int XDT, int TT, int TE, int UH = 4>
+__device__ __forceinline__ void router_block(const void* __restrict__ x, float sx, const float* __restrict__ wg,
+                                             int M, int E, int H, int t0, int e0, float (&acc)[TT][TE]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int e = 0; e < TE; ++e) acc[t][e] = 0.0f;
+#pragma unroll UH
+    for (int h0 = 4 * lane; h0 < H; h0 += 256) {
+        float4 w4[TE], x4[TT];
+#pragma unroll
+        for (int e = 0; e < TE; ++e)
+            w4[e] = (e0 + e < E) ? *reinterpret_cast<const float4*>(wg + (size_t)(e0 + e) * H + h0)
+                                 : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+            x4[t] = (t0 + t < M) ? router_x4<XDT>(x, (size_t)(t0 + t) * H + h0, sx) : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int e = 0; e < TE; ++e) {
+                float a = acc[t][e];
+                a = __builtin_fmaf(x4[t].x, w4[e].x, a);
+                a = __builtin_fmaf(x4[t].y, w4[e].y, a);
+                a = __builtin_fmaf(x4[t].z, w4[e].z, a);
+                acc[t][e] = __builtin_fmaf(x4[t].w, w4[e].w, a);
+            }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int e = 0; e < TE; ++e) {
+            float v = acc[t][e];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            acc[t][e] = v;
+        }
+}
+
+// One wavefront per block of TT tokens x TE experts, four per workgroup, no
+// LDS and no barrier (every load of a wavefront is independent of its other
+// loads, so they overlap).  The block shape only spreads the work: one
+// expert per wavefront while that makes fewer than 1024 blocks (more
+// wavefronts for few tokens), else 4 (each token row read a quarter as often).
+constexpr int kRtTT = 8;
+
+template <int XDT, int TE>
+__global__ void __launch_bounds__(256) router_logits_kernel(const void* __restrict__ x, const float* __restrict__ x_scale,
+                                                            const float* __restrict__ wg, int M, int E, int H,
+                                                            float* __restrict__ logits) {
+    const int eblocks = (E + TE - 1) / TE;
+    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= ((M + kRtTT - 1) / kRtTT) * eblocks) return;
+    const int t0 = (blk / eblocks) * kRtTT, e0 = (blk % eblocks) * TE;
+    const float sx = x_scale ? x_scale[0] : 1.0f;
+    float acc[kRtTT][TE];
+    router_block<XDT, kRtTT, TE>(x, sx, wg, M, E, H, t0, e0, acc);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < kRtTT; ++t)
+#pragma unroll
+        for (int e = 0; e < TE; ++e)
+            if (lane == t * TE + e && t0 + t < M && e0 + e < E) logits[(size_t)(t0 + t) * E + e0 + e] = acc[t][e];
+}
+
+template <int XDT>
+static hipError_t launch_router_x(const void* x, const float* x_scale, const float* wg, int M, int E, int H,
+                                  float* logits, hipStream_t s) {
+    const long tblocks = (M + kRtTT - 1) / kRtTT;
+    const int te = tblocks * E < 1024 ? 1 : 4;
+    const long blocks = (long)((M + kRtTT - 1) / kRtTT) * ((E + te - 1) / te);
+    const dim3 grid((unsigned)((blocks + 3) / 4));
+    if (te == 1)
+        hipLaunchKernelGGL((router_logits_kernel<XDT, 1>), grid, dim3(256), 0, s, x, x_scale, wg, M, E, H, logits);
+    else
+        hipLaunchKernelGGL((router_logits_kernel<XDT, 4>), grid, dim3(256), 0, s, x, x_scale, wg, M, E, H, logits);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_logits(moe_dtype xdt, const void* x, const float* x_scale, const float* wg, int M, int E,
+                                int H, float* logits, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    if (xdt == MOE_F32) return launch_router_x<MOE_F32>(x, x_scale, wg, M, E, H, logits, s);
+    if (xdt == MOE_BF16) return launch_router_x<MOE_BF16>(x, x_scale, wg, M, E, H, logits, s);
+    return launch_router_x<MOE_FP8_E4M3>(x, x_scale, wg, M, E, H, logits, s);
+}
+
+// A few tokens, inside the one-workgroup route + align launch: the 16
+// wavefronts take (4-token, 1-expert) blocks round robin (small blocks and a
+// short unroll: a 1024-thread workgroup has 128 registers per lane).
+template <int XDT>
+__device__ __forceinline__ void router_phase(const void* __restrict__ x, const float* __restrict__ x_scale,
+                                             const float* __restrict__ wg, int M, int E, int H, float* logits_s,
+                                             float* __restrict__ logits_out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float sx = x_scale ? x_scale[0] : 1.0f;
+    constexpr int TT = 4;
+    const int blocks = ((M + TT - 1) / TT) * E;
+    for (int blk = wave; blk < blocks; blk += kAlignWavesR) {
+        const int t0 = (blk / E) * TT, e0 = blk % E;
+        float acc[TT][1];
+        router_block<XDT, TT, 1, 2>(x, sx, wg, M, E, H, t0, e0, acc);
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+            if (lane == t && t0 + t < M) {
+                logits_s[(t0 + t) * E + e0] = acc[t][0];
+                if (logits_out) logits_out[(size_t)(t0 + t) * E + e0] = acc[t][0];
+            }
+    }
+}
+
 // ------------------------------------------------------------------ align
 //
 // min(ceil(P / 1024), 64) workgroups of 1024 threads, no inter-workgroup
@@ -139,6 +293,7 @@ hipError_t launch_route(const float* logits, int M, int E, int topk, int renorma
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
+static_assert(kAlignWaves == kAlignWavesR, "router phase wavefronts");
 constexpr int kMaxE = kMaxExperts;
 constexpr int kAlignMaxBlocks = 64;
 
@@ -311,27 +466,44 @@ __device__ __forceinline__ void align_core(GetId get_id, int P, int E, int block
 constexpr int kSmallMaxPairs = kAlignThreads;
 constexpr int kSmallMaxTiles = kAlignThreads;  // cap/block_m <= min(E,P) + P/block_m <= 1024 (see moe_align_capacity)
 
-template <bool ROUTE>
+// Router inputs of the MODE 2 launch (scores computed in the kernel).
+struct RouterIn {
+    const void* x;
+    const float* x_scale;
+    const float* wg;
+    int H;
+    float* logits_out;  // nullable
+};
+
+// MODE 0: ids given; 1: logits given (wavefront w routes token w); 2: router
+// weights given (the workgroup scores the tokens first, router_phase).
+template <int MODE, int XDT = MOE_BF16>
 __global__ void __launch_bounds__(kAlignThreads) align_small_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ ids_in, int M, int E, int topk, int renormalize,
     int32_t* __restrict__ ids_out, float* __restrict__ weights_out, int block_m, int cap,
     int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert, int32_t* __restrict__ counts_out,
     int32_t* __restrict__ offsets_out, int32_t* __restrict__ active, int32_t* __restrict__ num_active,
-    float* __restrict__ zero_f32) {
+    float* __restrict__ zero_f32, RouterIn rin) {
     __shared__ int ids_s[kSmallMaxPairs];
     __shared__ int wcnt[kAlignWaves][kMaxE];
     __shared__ int off_s[kMaxE + 1];
     __shared__ int cnt_s[kMaxE];
     __shared__ int tile_s[kSmallMaxTiles];
+    __shared__ float logits_s[MODE == 2 ? kRouteRouterMaxM * kMaxE : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = M * topk;
     if (tid == 0 && zero_f32) *zero_f32 = 0.0f;
     for (int i = tid; i < kAlignWaves * kMaxE; i += kAlignThreads) (&wcnt[0][0])[i] = 0;
-    if constexpr (ROUTE) {
+    if constexpr (MODE == 2) {
+        router_phase<XDT>(rin.x, rin.x_scale, rin.wg, M, E, rin.H, logits_s, rin.logits_out);
+        __syncthreads();
+    }
+    if constexpr (MODE >= 1) {
         if (wave < M) {
             int sel;
             float w;
-            route_token(logits + (size_t)wave * E, E, topk, renormalize, &sel, &w);
+            const float* row = (MODE == 2) ? logits_s + wave * E : logits + (size_t)wave * E;
+            route_token(row, E, topk, renormalize, &sel, &w);
             if (lane < topk) {
                 ids_out[(size_t)wave * topk + lane] = sel;
                 weights_out[(size_t)wave * topk + lane] = w;
@@ -441,9 +613,10 @@ hipError_t launch_align(const int32_t* ids, int M, int topk, int E, int block_m,
     if (M == 0) return hipSuccess;
     const int P = M * topk;
     if (P <= kSmallMaxPairs) {
-        hipLaunchKernelGGL((align_small_kernel<false>), dim3(1), dim3(kAlignThreads), 0, s, nullptr, ids, M, E, topk,
+        hipLaunchKernelGGL((align_small_kernel<0>), dim3(1), dim3(kAlignThreads), 0, s, nullptr, ids, M, E, topk,
                            1, nullptr, nullptr, block_m, (int)cap, out.sorted_ids, out.tile_expert,
-                           out.expert_counts, out.expert_offsets, out.active_experts, out.num_active, zero_f32);
+                           out.expert_counts, out.expert_offsets, out.active_experts, out.num_active, zero_f32,
+                           RouterIn{});
         return hipGetLastError();
     }
     // every workgroup reads all P ids, so their number is capped: past 64 K
@@ -470,9 +643,36 @@ hipError_t launch_route_align(const float* logits, int M, int E, int topk, int r
                               float* weights, int block_m, int64_t cap, const moe_align_bufs& out,
                               float* zero_f32, hipStream_t s) {
     if (!route_align_fits(M) || M * topk > kSmallMaxPairs) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((align_small_kernel<true>), dim3(1), dim3(kAlignThreads), 0, s, logits, nullptr, M, E, topk,
+    hipLaunchKernelGGL((align_small_kernel<1>), dim3(1), dim3(kAlignThreads), 0, s, logits, nullptr, M, E, topk,
                        renormalize, ids, weights, block_m, (int)cap, out.sorted_ids, out.tile_expert,
-                       out.expert_counts, out.expert_offsets, out.active_experts, out.num_active, zero_f32);
+                       out.expert_counts, out.expert_offsets, out.active_experts, out.num_active, zero_f32,
+                       RouterIn{});
+    return hipGetLastError();
+}
+
+// Router + route + align in one launch: a few tokens and a router matrix
+// small enough for one workgroup to stream.
+bool router_route_align_fits(int M, int E, int H) {
+    // the workgroup streams the router matrix once per 8-token block: at most
+    // 64 K weights and 128 K multiply-adds in all
+    return route_align_fits(M) && M <= kRouteRouterMaxM && (long)E * H <= 65536 && (long)M * E * H <= 131072 &&
+           H % 4 == 0;
+}
+
+hipError_t launch_router_route_align(moe_dtype xdt, const void* x, const float* x_scale, const float* wg, int H,
+                                     float* logits_out, int M, int E, int topk, int renormalize, int32_t* ids,
+                                     float* weights, int block_m, int64_t cap, const moe_align_bufs& out,
+                                     float* zero_f32, hipStream_t s) {
+    if (!router_route_align_fits(M, E, H) || M * topk > kSmallMaxPairs) return hipErrorInvalidValue;
+    const RouterIn rin{x, x_scale, wg, H, logits_out};
+#define MOE_RRA(XDT)                                                                                              \
+    hipLaunchKernelGGL((align_small_kernel<2, XDT>), dim3(1), dim3(kAlignThreads), 0, s, nullptr, nullptr, M, E,   \
+                       topk, renormalize, ids, weights, block_m, (int)cap, out.sorted_ids, out.tile_expert,         \
+                       out.expert_counts, out.expert_offsets, out.active_experts, out.num_active, zero_f32, rin)
+    if (xdt == MOE_F32) MOE_RRA(MOE_F32);
+    else if (xdt == MOE_BF16) MOE_RRA(MOE_BF16);
+    else MOE_RRA(MOE_FP8_E4M3);
+#undef MOE_RRA
     return hipGetLastError();
 }
 

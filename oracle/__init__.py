@@ -67,6 +67,7 @@ def lib():
             "oracle_pairs_gate_up": (i32, [i32, P, P, P, i64, i32, P, P, i32, i64, i64, P, i64, P]),
             "oracle_pairs_down": (i32, [i32, i32, P, dbl, P, i64, P, P, i32, i64, i64, P, i64, P]),
             "oracle_combine": (i32, [i32, P, P, i64, i32, i64, P]),
+            "oracle_router_logits": (i32, [i32, P, P, P, i64, i32, i64, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -130,6 +131,18 @@ def route(logits, topk: int, renormalize: bool = True):
     w = np.empty((M, topk), np.float64)
     _check(lib().oracle_route(_ptr(lg), M, E, topk, int(renormalize), _ptr(ids), _ptr(w)), "route")
     return ids, w
+
+
+def router_logits(dtype, x, x_scale, wg):
+    """float64 [M, E] = x . wg^T (wg float32 [E, H]; x stored as dtype, times x_scale)."""
+    xn = _np(x)
+    wgn = np.ascontiguousarray(_np(wg), np.float32)
+    M, H = xn.shape
+    E = wgn.shape[0]
+    out = np.empty((M, E), np.float64)
+    _check(lib().oracle_router_logits(_DT[dtype], _ptr(xn), _ptr(_f32(x_scale)), _ptr(wgn), M, E, H, _ptr(out)),
+           "router_logits")
+    return out
 
 
 def align_capacity(M: int, topk: int, E: int, block_m: int) -> int:

@@ -163,6 +163,31 @@ int oracle_route(const float* logits, int64_t M, int E, int k, int renorm, int32
     return OR_OK;
 }
 
+/* The router (FusedMoE vs MegaMoE post, section 2: the router yields one
+ * score per expert for each token): logits[t][e] = sum_h x[t][h] * wg[e][h],
+ * x widened from its storage (times its scale), wg float32 [E][H]. */
+int oracle_router_logits(int dtype, const void* x, const float* x_scale, const float* wg, int64_t M, int E,
+                         int64_t H, double* logits) {
+    if (M < 0 || E < 1 || H < 1) return OR_EARG;
+    size_t eb = dtype == OR_F32 ? 4 : dtype == OR_BF16 ? 2 : 1;
+    double xs = x_scale ? (double)x_scale[0] : 1.0;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < M; ++t) {
+        const char* row = (const char*)x + (size_t)t * H * eb;
+        for (int e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                double xv = dtype == OR_F32   ? (double)((const float*)row)[h]
+                            : dtype == OR_BF16 ? oracle_bf16_decode(((const uint16_t*)row)[h])
+                                               : oracle_e4m3_decode(((const uint8_t*)row)[h]);
+                s += xv * xs * (double)wg[(size_t)e * H + h];
+            }
+            logits[t * E + e] = s;
+        }
+    }
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------- alignment */
 
 int64_t oracle_align_capacity(int64_t M, int k, int E, int bm) {

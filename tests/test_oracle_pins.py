@@ -366,3 +366,27 @@ def test_fp8_golden_amax_single_token_recomputes():
     w = layer_weights(cfg, "cpu", experts=sorted(set(ids.reshape(-1).tolist())))
     am = oracle.act_amax("fp8", b["x"], b["x_scale"], b["logits"], w["w1"], w["w1_scale"], cfg.topk)
     assert am == gold["amax"]["1"]
+
+
+# ---------------------------------------------------------------- router
+
+def test_router_logits_vs_numpy_matmul():
+    """oracle.router_logits against numpy's float64 matmul of the widened
+    inputs, for float32, bfloat16 and e4m3 (times its scale) activations."""
+    from workloads.gen import _quant_e4m3_per_tensor
+    rng = np.random.default_rng(41)
+    M, E, H = 9, 12, 96
+    x = rng.standard_normal((M, H)).astype(np.float32)
+    wg = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    ref = x.astype(np.float64) @ wg.astype(np.float64).T
+    np.testing.assert_allclose(oracle.router_logits("f32", x, None, wg), ref, rtol=1e-12, atol=1e-14)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    refb = xb.double().numpy() @ wg.astype(np.float64).T
+    np.testing.assert_allclose(oracle.router_logits("bf16", xb, None, wg), refb, rtol=1e-12, atol=1e-14)
+    xq, sx = _quant_e4m3_per_tensor(torch.from_numpy(x))
+    refq = (xq.double().numpy() * float(sx)) @ wg.astype(np.float64).T
+    np.testing.assert_allclose(oracle.router_logits("fp8", xq, sx, wg), refq, rtol=1e-12, atol=1e-14)
+    # a one-hot router row picks that activation column
+    wg1 = np.zeros((E, H), np.float32)
+    wg1[3, 17] = 1.0
+    assert np.array_equal(oracle.router_logits("f32", x, None, wg1)[:, 3], x[:, 17].astype(np.float64))
