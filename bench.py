@@ -34,11 +34,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA peaks
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "w4a16": 2500.0}  # dense MFMA peaks (W4A16: bf16)
+# bytes per weight (W4A16: a 4-bit code and 1/128 of a float32 scale) and per activation
+W_BYTES = {"bf16": 2, "fp8": 1, "f32": 4, "w4a16": 0.5 + 4 / 128}
+X_BYTES = {"bf16": 2, "fp8": 1, "f32": 4, "w4a16": 2}
+DTYPE_NAME = {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32", "w4a16": "int4_weights_bf16_act"}
 METRIC = "MoE layer tokens/s; decode HBM GB/s & prefill MFMA TFLOP/s as % of peak"
 
 MAIN = ("mixtral_decode_bf16", 64)
-EXTRA = (("mixtral_prefill_bf16", 4096), ("fp8_e4m3", 32))
+EXTRA = (("mixtral_prefill_bf16", 4096), ("fp8_e4m3", 32), ("mixtral_decode_w4a16", 64))
 MAIN_SWEEP = (1, 8, 32)
 
 
@@ -68,9 +72,9 @@ def layer_bytes(cfg, M, n_active, wbytes, xbytes, obytes):
 
 
 def act_elem_bytes(cfg):
-    """Bytes per element of the stored intermediate: bf16 for the bf16 layer,
-    float32 for the f32 and e4m3 layers."""
-    return 2 if cfg.dtype == "bf16" else 4
+    """Bytes per element of the stored intermediate: bf16 for the bf16 and
+    W4A16 layers, float32 for the f32 and e4m3 layers."""
+    return 2 if cfg.dtype in ("bf16", "w4a16") else 4
 
 
 def gate_up_bytes(cfg, M, n_active, wbytes, xbytes):
@@ -89,6 +93,8 @@ def down_bytes(cfg, M, n_active, wbytes, act_bytes):
 
 def fused_block_m(cfg, M):
     """The tile height fused_moe picks for a batch (the library's rule)."""
+    if cfg.dtype in ("f32", "w4a16"):
+        return 16
     pe = (M * cfg.topk) // cfg.E
     return 128 if pe > (32 if cfg.dtype == "fp8" else 64) else 16
 
@@ -200,7 +206,7 @@ def measure(moe, torch, np, cfg, w, M, steps, warmup, dev, events=True):
     from workloads import layer_batch
     b = layer_batch(cfg, M, dev)
     I, H, E, k = cfg.I, cfg.H, cfg.E, cfg.topk
-    wb = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.dtype]
+    wb, xb = W_BYTES[cfg.dtype], X_BYTES[cfg.dtype]
     ob = 4 if cfg.dtype == "f32" else 2
     dt = moe.moe_dtype(w["w1"])
     ws = torch.empty(moe.fused_moe_workspace_size(dt, M, E, k, H, I), dtype=torch.uint8, device=dev)
@@ -221,7 +227,7 @@ def measure(moe, torch, np, cfg, w, M, steps, warmup, dev, events=True):
     fused_s = (time.perf_counter() - t) / steps
     n_active = int(torch.unique(ids).numel())
     res = {"M": M, "ms_per_step": fused_s * 1e3, "tokens_per_s": M / fused_s, "active_experts": n_active}
-    lb = layer_bytes(cfg, M, n_active, wb, wb, ob)
+    lb = layer_bytes(cfg, M, n_active, wb, xb, ob)
     fl = 6.0 * M * k * H * I
     peak_f = MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12
     res["layer_bytes"], res["layer_flops"] = lb, fl
@@ -321,7 +327,7 @@ def measure(moe, torch, np, cfg, w, M, steps, warmup, dev, events=True):
     res["staged_ms_per_step"] = (time.perf_counter() - t) / steps * 1e3
     ms = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(nk)] for s in range(steps)])
     res["kernel_us"] = {n: float(ms[:, i].mean() * 1e3) for i, n in enumerate(names)}
-    res["gate_up_bytes"] = gate_up_bytes(cfg, M, n_active, wb, wb)
+    res["gate_up_bytes"] = gate_up_bytes(cfg, M, n_active, wb, xb)
     res["gate_up_flops"] = 4.0 * M * k * H * I
     res["gate_up_GBs"] = res["gate_up_bytes"] / (res["kernel_us"]["gate_up"] * 1e-6) / 1e9
     res["gate_up_TFLOPs"] = res["gate_up_flops"] / (res["kernel_us"]["gate_up"] * 1e-6) / 1e12
@@ -387,7 +393,7 @@ def line_entry(cfg, res, cpu):
     keys = ("ms_per_step", "tokens_per_s", "roofline_frac", "layer_hbm_frac", "layer_mfma_frac", "cold_ms_per_step",
             "cold_p10_p90_ms", "cold_roofline_frac", "graph_ms_per_step", "staged_ms_per_step", "kernel_us",
             "gate_up_GBs", "gate_up_TFLOPs", "down_GBs", "down_TFLOPs", "active_experts")
-    e = {"workload": cfg.name, "M": res["M"], "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32"}[cfg.dtype],
+    e = {"workload": cfg.name, "M": res["M"], "dtype": DTYPE_NAME[cfg.dtype],
          "E": cfg.E, "topk": cfg.topk, "hidden": cfg.H, "intermediate": cfg.I}
     e.update({k2: res[k2] for k2 in keys if k2 in res})
     e["roofline"] = roofline(cfg, res)
@@ -444,6 +450,8 @@ def main():
 
     def weights_for(cfg):
         key = (cfg.E, cfg.H, cfg.I, cfg.dtype)  # the prefill and decode Mixtral layers share their weights
+        if cfg.dtype == "w4a16":
+            weights.clear()  # free the bf16/e4m3 layers first
         if key not in weights:
             t0 = time.time()
             weights[key] = layer_weights(cfg, dev)
@@ -484,7 +492,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32"}[main_cfg.dtype],
+        "dtype": DTYPE_NAME[main_cfg.dtype],
         "data": "synthetic (seeded counter-based normals; random-init weights)",
         "config": {"workload": main_cfg.name, "M": main_M, "E": main_cfg.E, "topk": main_cfg.topk,
                    "hidden": main_cfg.H, "intermediate": main_cfg.I, "parallelism": "single GPU"},

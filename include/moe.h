@@ -48,7 +48,9 @@ typedef enum {
 typedef enum {
     MOE_F32 = 0,     /* IEEE binary32                                          */
     MOE_BF16 = 1,    /* bfloat16                                               */
-    MOE_FP8_E4M3 = 2 /* OCP OFP8 E4M3 (bias 7, max 448, no inf) + float32 scale */
+    MOE_FP8_E4M3 = 2, /* OCP OFP8 E4M3 (bias 7, max 448, no inf) + float32 scale */
+    MOE_W4A16 = 3     /* weights: 4-bit codes with a float32 scale per 128 k of a row;
+                         activations and outputs bfloat16 (see moe_grouped_gemm) */
 } moe_dtype;
 
 typedef enum {
@@ -138,6 +140,15 @@ moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t E
  *         are quantised on load with one per-tensor scale s = amax/448: code
  *         = e4m3(act / s), IEEE float32 quotient, round to nearest even,
  *         saturating at +-448; c = y bfloat16).
+ *         MOE_W4A16 (weight-only int4; FusedMoE vs MegaMoE post, sections
+ *         6.2-6.3): a and c bfloat16 as for MOE_BF16; w = uint8 [E][N][K/2]
+ *         codes, w_scale -> float32 [E][K/128][N] scales (group-major), and
+ *         W[e][n][k] = (u - 8) * w_scale[e][k/128][n] for the 4-bit code u of
+ *         (n, k): the codes of 8 consecutive k (k0 a multiple of 8) fill one
+ *         little-endian 32-bit word, k0+2i at bits 4i..4i+3 and k0+2i+1 at
+ *         bits 16+4i..16+4i+3; K must be a multiple of 256.  Served by the
+ *         decode kernel at every batch size (a batch with many rows per
+ *         expert streams the weights once per 32 of them).
  *  kind = MOE_GEMM_DOWN_E4M3_ACT (MOE_FP8_E4M3 only): as MOE_GEMM_DOWN, but a
  *         holds the e4m3 codes [P][K] that moe_quant_act wrote for the same
  *         amax, and a_scale -> that amax.  Same codes, same scales, same
@@ -179,14 +190,17 @@ size_t fused_moe_workspace_size(moe_dtype dtype, int32_t M, int32_t E, int32_t t
 
 /* The whole layer: route -> align -> GATE_UP GEMM -> DOWN GEMM -> combine, all
  * on `stream`, no host synchronisation.
- *  x              device [M][H]: float32, bfloat16 or e4m3 (x_scale -> float32)
+ *  x              device [M][H]: float32, bfloat16 (also for MOE_W4A16) or e4m3
+ *                 (x_scale -> float32)
  *  router_logits  device float32 [M][E]
  *  w1, w2         device [E][2I][H] and [E][H][I] in dtype (fp8: w1_scale,
- *                 w2_scale device float32 [E])
+ *                 w2_scale device float32 [E]; MOE_W4A16: packed codes
+ *                 [E][2I][H/2] and [E][H][I/2], w1_scale [E][H/128][2I],
+ *                 w2_scale [E][I/128][H], as for moe_grouped_gemm)
  *  out            device [M][H]: float32 for MOE_F32, bfloat16 otherwise
  *  topk_ids_out, topk_weights_out  optional device [M][topk] copies of the
  *                 routing result (NULL to skip)
- *  H and I must be multiples of 128 (of 256 for MOE_FP8_E4M3).
+ *  H and I must be multiples of 128 (of 256 for MOE_FP8_E4M3 and MOE_W4A16).
  *  workspace      device, >= fused_moe_workspace_size(...) bytes, 256-byte
  *                 aligned; its contents on entry do not matter. */
 moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,

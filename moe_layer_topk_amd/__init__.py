@@ -19,6 +19,7 @@ import torch
 
 from ._lib import (  # noqa: F401
     MOE_ERR_SCRATCH,
+    MOE_W4A16,
     MOE_BF16,
     MOE_F32,
     MOE_FP8_E4M3,
@@ -31,9 +32,12 @@ from ._lib import (  # noqa: F401
     lib,
 )
 
-_DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3}
-_INTER = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.bfloat16}  # y and out
-_ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.float32}  # the intermediate
+# weight storage -> layer dtype (uint8 weights are packed int4 codes, W4A16)
+_DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3, torch.uint8: MOE_W4A16}
+_INTER = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.bfloat16,
+          MOE_W4A16: torch.bfloat16}  # y and out
+_ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.float32,
+        MOE_W4A16: torch.bfloat16}  # the intermediate
 
 
 def _p(t):
@@ -98,6 +102,8 @@ def moe_grouped_gemm(kind: int, a: torch.Tensor, w: torch.Tensor, al: dict, M: i
     """GATE_UP: act[P, N/2] = silu(gate) * up;  DOWN: y[P, N].  Returns (c, c_amax)."""
     E, N, K = w.shape
     dt = moe_dtype(w)
+    if dt == MOE_W4A16:
+        K *= 2  # two 4-bit codes per byte
     P = M * topk
     cols = N // 2 if kind == MOE_GEMM_GATE_UP_SILU else N
     if kind != MOE_GEMM_GATE_UP_SILU and (kind == MOE_GEMM_DOWN_E4M3_ACT) != (a.dtype == torch.float8_e4m3fn):

@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 (MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_ALIGNMENT, MOE_ERR_HIP,
  MOE_ERR_SCRATCH) = range(8)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_W4A16 = 0, 1, 2, 3
 MOE_GEMM_GATE_UP_SILU, MOE_GEMM_DOWN, MOE_GEMM_DOWN_E4M3_ACT = 0, 1, 2
 
 

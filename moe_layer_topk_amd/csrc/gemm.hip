@@ -1340,6 +1340,300 @@ static hipError_t launch_decode_ring(const GemmArgs& a, int nslots, hipStream_t 
     return hipGetLastError();
 }
 
+// ------------------------------------------- decode, int4 weights (W4A16)
+//
+// Weight-only int4 (FusedMoE vs MegaMoE post, sections 6.2-6.3: INT4 weights
+// cut the memory the expert GEMMs stream).  W[n][k] = (u - 8) * s[k/128][n]:
+// 4-bit codes u packed so that the 32-bit word of 8 consecutive k holds
+// k0+2i at bits 4i and k0+2i+1 at bits 16+4i, and one float32 scale per
+// 128-wide group of k of a row, stored group-major.  Activations are bf16.
+//
+// The decode work split of the ring kernel (blockIdx.y active-expert slot,
+// blockIdx.x G groups of 64 weight rows, blockIdx.z K split; the four
+// wavefronts take steps round robin and reduce through LDS at the end).  A
+// step is 128 bytes of every weight row (256 k, two scale groups); the codes
+// stream through a wavefront-private LDS ring of direct-to-LDS copies (as
+// in the ring kernel, non-temporal), one more copy per stage brings the
+// step's group scales of the 64 rows.  The token values of a step (bf16)
+// come through registers two steps ahead, as in the ring kernel's e4m3
+// down projection: the loads of step j+2 follow the wait that retires step
+// j's copies, and the scale copy of step j+2 follows them (into step j's
+// slot, whose reads are done), so the only copies younger than a step's
+// token loads when they are consumed are the next stage's 8 weight copies,
+// which the compiler's own wait (it counts the 8 younger token loads) leaves
+// in flight.
+//
+// Products on the bf16 MFMA without converting codes to values: OR-ing a
+// code into 0x4300 gives the bf16 128 + u exactly, so one AND-OR turns a
+// word of codes into two bf16 operand words, and for a group g
+//   sum_k W[n][k] x[k] = s[g][n] * (sum_k (128 + u_k) x_k - 136 * sum_k x_k),
+// the token sums coming from an MFMA with an all-ones operand.  Each MFMA
+// covers 32 k of one group (lane group lg: k = 128 g + 32 lg + 8 q + j), so
+// every group's products are accumulated apart and scaled per row.
+
+template <int KIND, int NT, int G, int KD>
+__global__ void __launch_bounds__(kDecThreads) gemm_decode_w4_kernel(GemmArgs g) {
+    constexpr int T = 4;                      // 16-row tiles per group of 64 rows
+    constexpr int kWInstr = 64 * kRingSB / 1024;
+    constexpr int kScaleOff = 64 * kRingSB;   // [2 groups][64 rows] float32 after the codes
+    constexpr int kStage = 64 * kRingSB + 1024;
+    static_assert(KD == 2, "the scale copy of step j+2 goes to step j's slot");
+    extern __shared__ __attribute__((aligned(1024))) char w4_lds[];
+
+    const int slot = blockIdx.y;
+    if (slot >= *g.num_active) return;
+    const int e = g.active[slot];
+    const int cnt = g.counts[e];
+    const int base = g.offsets[e];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int drow = lane >> 3, dpc = lane & 7;
+    const int K = g.K, N = g.N, I = N / 2;
+    const size_t rowb = (size_t)K / 2;  // packed codes per row
+    const int nks_all = (int)(rowb / kRingSB);
+    const int ks0 = (int)((long)blockIdx.z * nks_all / g.ksplit);
+    const int nks = (int)((long)(blockIdx.z + 1) * nks_all / g.ksplit) - ks0;
+    const int total = G * nks;
+    const int nw = total > wave ? (total - wave + 3) / 4 : 0;
+
+    const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 32 * G : blockIdx.x * 64 * G;
+    const int grows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 : 64;  // row offset between this block's groups
+    const char* wexp = reinterpret_cast<const char*>(g.w) + (size_t)e * N * rowb;
+    size_t woff[kWInstr];
+#pragma unroll
+    for (int i = 0; i < kWInstr; ++i) {
+        const int ri = 8 * i + drow;
+        const int row = (KIND == MOE_GEMM_GATE_UP_SILU) ? ((ri < 32) ? n0 + ri : I + n0 + ri - 32) : n0 + ri;
+        woff[i] = (size_t)row * rowb + ring_swz(dpc, ri) * 16;
+    }
+    // the scale copy: lane l (mod 32) brings 4 scales of group (l / 16) of the
+    // step, rows 4 (l % 16).. of the 64 (gate rows then up rows for GATE_UP),
+    // to LDS bytes 16 l: the [group][row] layout the MFMA epilogues read
+    const float* sexp = g.w_scale + (size_t)e * (K / 128) * N;
+    const int sl = lane & 31, skg = sl >> 4, sq = sl & 15;
+    const int srow = (KIND == MOE_GEMM_GATE_UP_SILU) ? ((sq < 8) ? n0 + 4 * sq : I + n0 + 4 * (sq - 8)) : n0 + 4 * sq;
+
+    char* ring = w4_lds + wave * (KD * kStage);
+    const unsigned ring_lds0 = lds_addr_of(ring);
+    f32x4* red = reinterpret_cast<f32x4*>(w4_lds);  // after the main loop only
+    const uint4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
+
+    for (int pass = 0; pass < cnt; pass += NT * 16) {
+        const int ntiles = min(NT, (cnt - pass + 15) / 16);
+        // this lane's token rows (rows past the count repeat the last one) at
+        // its lane group's 32 values of each 128-value group
+        const char* trow[NT];
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int p = g.sorted[base + min(pass + 16 * c + lr, cnt - 1)];
+            const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
+            trow[c] = reinterpret_cast<const char*>(g.a) + (size_t)src * K * 2 + 64 * lg;
+        }
+        // the codes of step j (8 copies)
+        auto issue = [&](int j) {
+            const int s = wave + 4 * j;
+            const int gi = s / nks, ks = ks0 + s % nks;
+            const unsigned st = ring_lds0 + (unsigned)((j % KD) * kStage);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const char* wsrc = wexp + (size_t)gi * grows * rowb + (size_t)ks * kRingSB;
+#pragma unroll
+            for (int i = 0; i < kWInstr; ++i) lds_dma16_nt_at(wsrc + woff[i], st + i * 1024);
+        };
+        // the group scales of step j (one copy)
+        auto issue_scales = [&](int j) {
+            const int s = wave + 4 * j;
+            const int gi = s / nks, ks = ks0 + s % nks;
+            const unsigned st = ring_lds0 + (unsigned)((j % KD) * kStage);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            lds_dma16_at(sexp + (size_t)(2 * ks + skg) * N + srow + gi * grows, st + kScaleOff);
+        };
+        // the bf16 token values of step j: 8 x 16 bytes per tile (values
+        // 128 kg + 32 lg + 8 q .. + 7 of the step, kg = 0..1, q = 0..3)
+        auto tload = [&](uint4 (&b)[NT][8], int j) {
+            const int ks = ks0 + (wave + 4 * j) % nks;
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                const char* src = trow[c] + (size_t)ks * (2 * 2 * kRingSB);
+#pragma unroll
+                for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) b[c][4 * kg + q] = *reinterpret_cast<const uint4*>(src + 256 * kg + 16 * q);
+            }
+        };
+
+        f32x4 acc[G][T][NT];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int c = 0; c < NT; ++c) acc[gi][t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        uint4 tb0[NT][8], tb1[NT][8];
+        tload(tb0, 0);
+        tload(tb1, nw > 1 ? 1 : 0);
+        if (0 < nw) {
+            issue(0);
+            issue_scales(0);
+        }
+        if (1 < nw) issue_scales(1);
+
+        auto step = [&](int j, uint4 (&tb)[NT][8]) {
+            if (j + 1 < nw) {
+                issue(j + 1);
+                ring_wait_vm<kWInstr>();
+            } else {
+                ring_wait_vm<0>();
+            }
+            // every vector-memory operation older than the copies just issued
+            // has completed: this step's codes, scales and token values
+            const char* st = ring + (j % KD) * kStage;
+            const float* sc = reinterpret_cast<const float*>(st + kScaleOff);
+            const int gi = (wave + 4 * j) / nks;
+            const int sw = (lr >> 1) & 7;
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg) {
+                if (gg != gi) continue;
+#pragma unroll
+                for (int kg = 0; kg < 2; ++kg) {
+                    f32x4 xs[NT];
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) {
+                        xs[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (c < ntiles)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) xs[c] = Opnd<MOE_BF16>::mfma(ones, tb[c][4 * kg + q], xs[c]);
+                    }
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        const uint4 wq =
+                            *reinterpret_cast<const uint4*>(st + (16 * t + lr) * kRingSB + (((4 * kg + lg) ^ sw) << 4));
+                        const f32x4 s4 = *reinterpret_cast<const f32x4*>(sc + kg * 64 + 16 * t + 4 * lg);
+                        const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+                        for (int c = 0; c < NT; ++c) {
+                            if (c < ntiles) {
+                                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const uint32_t w = wd[q];
+                                    const uint4 av = {(w & 0x000F000Fu) | 0x43004300u,
+                                                      ((w >> 4) & 0x000F000Fu) | 0x43004300u,
+                                                      ((w >> 8) & 0x000F000Fu) | 0x43004300u,
+                                                      ((w >> 12) & 0x000F000Fu) | 0x43004300u};
+                                    a = Opnd<MOE_BF16>::mfma(av, tb[c][4 * kg + q], a);
+                                }
+#pragma unroll
+                                for (int v = 0; v < 4; ++v)
+                                    acc[gg][t][c][v] = __builtin_fmaf(s4[v], a[v] - 136.0f * xs[c][v], acc[gg][t][c][v]);
+                            }
+                        }
+                    }
+                }
+            }
+            // refill this buffer with step j + 2's values (the last steps reload
+            // step nw-1, unused: a conditional refill would merge register
+            // states), then step j + 2's scales into this step's slot
+            tload(tb, min(j + 2, nw - 1));
+            if (j + 2 < nw) issue_scales(j + 2);
+        };
+        int j = 0;
+        for (; j + 1 < nw; j += 2) {
+            step(j, tb0);
+            step(j + 1, tb1);
+        }
+        if (j < nw) step(j, tb0);
+
+        // every wave is done with its ring: the reduction area aliases it
+        __syncthreads();
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int c = 0; c < NT; ++c) red[((wave * G * T + gi * T + t) * NT + c) * 64 + lane] = acc[gi][t][c];
+        __syncthreads();
+
+        constexpr int kPer = (KIND == MOE_GEMM_GATE_UP_SILU) ? 2 : 4;  // output tiles per group
+        const int units = G * kPer * ntiles;
+        for (int u = wave; u < units; u += 4) {
+            const int c = u / (G * kPer);
+            const int gq = u % (G * kPer);
+            const int gi = gq / kPer, q = gq % kPer;
+            const int r = pass + c * 16 + lr;
+            if (r >= cnt) continue;
+            const int p = g.sorted[base + r];
+            if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+                f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    gs += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
+                    us += red[((w * G * T + gi * T + q + 2) * NT + c) * 64 + lane];
+                }
+                float o[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[v] = silu(gs[v]) * us[v];
+                uint2 pk;
+                pk.x = pack_bf2(o[0], o[1]);
+                pk.y = pack_bf2(o[2], o[3]);
+                const int n = n0 + gi * 32 + 16 * q + 4 * lg;
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * I + n) = pk;
+            } else {
+                f32x4 ys = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) ys += red[((w * G * T + gi * T + q) * NT + c) * 64 + lane];
+                const int n = n0 + gi * 64 + 16 * q + 4 * lg;
+                if (g.cpart) {
+                    *reinterpret_cast<f32x4*>(g.cpart + ((size_t)blockIdx.z * g.P + p) * N + n) = ys;
+                } else {
+                    uint2 pk;
+                    pk.x = pack_bf2(ys[0], ys[1]);
+                    pk.y = pack_bf2(ys[2], ys[3]);
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.c) + (size_t)p * N + n) = pk;
+                }
+            }
+        }
+        // the next pass refills the rings over the reduction area
+        __syncthreads();
+    }
+}
+
+template <int KIND, int NT, int G>
+static hipError_t launch_decode_w4_g(const GemmArgs& a, int nslots, hipStream_t s) {
+    constexpr int KD = 2;
+    constexpr int kRing = 4 * KD * (64 * kRingSB + 1024);
+    constexpr int kRed = 4 * G * 4 * NT * 64 * 16;
+    constexpr int kLds = kRing > kRed ? kRing : kRed;
+    static_assert(kLds <= 160 * 1024, "LDS");
+    const int rows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 * G : 64 * G;
+    const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_w4_kernel<KIND, NT, G, KD>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gemm_decode_w4_kernel<KIND, NT, G, KD>), dim3(ncols / rows, nslots, a.ksplit),
+                       dim3(kDecThreads), kLds, s, a);
+    return hipGetLastError();
+}
+
+template <int KIND, int NT>
+static hipError_t launch_decode_w4_nt(const GemmArgs& a, int nslots, hipStream_t s) {
+    // an int4 row holds a quarter of a bf16 row's bytes: the gate/up GEMM takes
+    // four row groups per workgroup with one token tile (as many copy steps
+    // per wavefront as bf16 with one group), two with two tiles (registers);
+    // the down GEMM two when that still leaves 256 workgroups
+    const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
+    if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+        if (a.ksplit == 1 && ncols % 128 == 0) return launch_decode_w4_g<KIND, NT, NT == 1 ? 4 : 2>(a, nslots, s);
+    } else {
+        if (a.ksplit == 1 && ncols % 128 == 0 && (long)(ncols / 128) * nslots >= 256)
+            return launch_decode_w4_g<KIND, NT, 2>(a, nslots, s);
+    }
+    return launch_decode_w4_g<KIND, NT, 1>(a, nslots, s);
+}
+
 // ------------------------------------------------------------------- f32
 //
 // Plain fp32 path: one thread per (sorted row, output column), dot products
@@ -1392,7 +1686,9 @@ int down_ksplit(moe_dtype dtype, int M, int topk, int E, int N, int K, int block
     // layer at one token runs 6% faster in 2 splits than in 6, the
     // 128-expert one 10% faster unsplit than in 2)
     if (wgs >= 256) return 1;
-    const int steps = (int)((long)K * (dtype == MOE_BF16 ? 2 : 1) / kDecSpan);
+    // 256-byte steps of a weight row
+    const long rowb = dtype == MOE_BF16 ? 2L * K : dtype == MOE_W4A16 ? K / 2 : (long)K;
+    const int steps = (int)(rowb / kDecSpan);
     int ks = (int)((256 + wgs - 1) / wgs);
     if (ks > kMaxKsplit) ks = kMaxKsplit;
     // at least three 256-byte steps per split
@@ -1401,6 +1697,7 @@ int down_ksplit(moe_dtype dtype, int M, int topk, int E, int N, int K, int block
 }
 
 GemmPath choose_gemm_path(const GemmCall& g) {
+    if (g.dtype == MOE_W4A16) return GemmPath::kDecode;  // the int4 kernel is a decode kernel
     const char* env = getenv("MOE_GEMM_PATH");
     const bool pre_ok = prefill_supported_block_m(g.block_m);
     if (env && strcmp(env, "decode") == 0) return GemmPath::kDecode;
@@ -1525,7 +1822,17 @@ static hipError_t launch_prefill(const GemmArgs& a, int block_m, int64_t cap, hi
 }
 
 template <int KIND>
+static hipError_t launch_decode_w4(const GemmArgs& a, int M, int topk, int E, hipStream_t s) {
+    const long P = (long)M * topk;
+    const int nslots = (int)(P < E ? P : E);
+    // one or two 16-row token tiles per pass (more rows per expert: more passes)
+    if (decode_token_tiles(M, topk, E) == 1) return launch_decode_w4_nt<KIND, 1>(a, nslots, s);
+    return launch_decode_w4_nt<KIND, 2>(a, nslots, s);
+}
+
+template <int KIND>
 static hipError_t launch_kind(const GemmCall& c, const GemmArgs& a, int64_t cap, hipStream_t s) {
+    if (c.dtype == MOE_W4A16) return launch_decode_w4<KIND>(a, c.M, c.topk, c.E, s);
     if (c.dtype == MOE_F32 && choose_gemm_path(c) == GemmPath::kDecode)
         return launch_decode<KIND, MOE_F32>(a, c.M, c.topk, c.E, s);
     if (c.dtype == MOE_F32) {

@@ -28,17 +28,20 @@ moe_status check_router(int32_t M, int32_t E, int32_t topk) {
 
 bool valid_block_m(int32_t b) { return b == 1 || b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
 
-size_t elem_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : d == MOE_BF16 ? 2 : 1; }
+bool known_dtype(moe_dtype d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_FP8_E4M3 || d == MOE_W4A16; }
+
+// layer dtypes whose weights carry scales (fp8: one per expert matrix; W4A16: per group)
+bool scaled_weights(moe_dtype d) { return d == MOE_FP8_E4M3 || d == MOE_W4A16; }
 
 // bytes of an element of y: f32 for the f32 path, bf16 otherwise
 size_t inter_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : 2; }
 // ... and of act: the e4m3 layer keeps it in float32 until it is quantised
-size_t act_bytes(moe_dtype d) { return d == MOE_BF16 ? 2 : 4; }
+size_t act_bytes(moe_dtype d) { return (d == MOE_BF16 || d == MOE_W4A16) ? 2 : 4; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int32_t fused_block_m(moe_dtype dtype, int32_t M, int32_t E, int32_t topk) {
-    if (dtype == MOE_F32) return 16;
+    if (dtype == MOE_F32 || dtype == MOE_W4A16) return 16;  // decode kernels only
     const char* env = getenv("MOE_GEMM_PATH");
     if (env && strcmp(env, "prefill") == 0) return 64;
     if (env && strcmp(env, "decode") == 0) return 16;
@@ -161,7 +164,7 @@ moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, 
                             float* c_amax, void* stream) {
     if (kind != MOE_GEMM_GATE_UP_SILU && kind != MOE_GEMM_DOWN && kind != MOE_GEMM_DOWN_E4M3_ACT)
         return MOE_ERR_UNSUPPORTED;
-    if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if (!known_dtype(dtype)) return MOE_ERR_UNSUPPORTED;
     if (kind == MOE_GEMM_DOWN_E4M3_ACT && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
     const bool act_q8 = kind == MOE_GEMM_DOWN_E4M3_ACT;
     if (act_q8) kind = MOE_GEMM_DOWN;
@@ -170,15 +173,17 @@ moe_status moe_grouped_gemm(moe_gemm_kind kind, moe_dtype dtype, const void* a, 
     if (N < 1 || K < 1 || N % 128 || K % 128) return MOE_ERR_SHAPE;
     if (kind == MOE_GEMM_GATE_UP_SILU && N % 256) return MOE_ERR_SHAPE;
     if (!valid_block_m(block_m)) return MOE_ERR_UNSUPPORTED;
-    const bool fp8 = dtype == MOE_FP8_E4M3;
-    if (fp8 && K % 256) return MOE_ERR_SHAPE;
-    if (!fp8 && (a_scale || w_scale || c_amax)) return MOE_ERR_UNSUPPORTED;
+    const bool fp8 = dtype == MOE_FP8_E4M3, w4 = dtype == MOE_W4A16;
+    if ((fp8 || w4) && K % 256) return MOE_ERR_SHAPE;
+    if (!fp8 && (a_scale || c_amax)) return MOE_ERR_UNSUPPORTED;
+    if (!scaled_weights(dtype) && w_scale) return MOE_ERR_UNSUPPORTED;
     if (M == 0) return MOE_OK;
     if (!a || !w || !al || !c || !al->sorted_ids || !al->tile_expert || !al->expert_counts ||
         !al->expert_offsets || !al->active_experts || !al->num_active)
         return MOE_ERR_NULL;
     if (fp8 && (!a_scale || !w_scale || (kind == MOE_GEMM_GATE_UP_SILU && !c_amax))) return MOE_ERR_NULL;
-    if (misaligned(a) || misaligned(w) || misaligned(c)) return MOE_ERR_ALIGNMENT;
+    if (w4 && !w_scale) return MOE_ERR_NULL;
+    if (misaligned(a) || misaligned(w) || misaligned(c) || misaligned(w_scale)) return MOE_ERR_ALIGNMENT;
     GemmCall g{kind, dtype, a, a_scale, w, w_scale, *al, M, topk, E, N, K, block_m, c, c_amax, 1, nullptr, act_q8};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (fp8 && kind == MOE_GEMM_GATE_UP_SILU) {
@@ -223,18 +228,20 @@ moe_status check_fused(moe_dtype dtype, const void* x, const float* x_scale, con
                        const void* w1, const float* w1_scale, const void* w2, const float* w2_scale, int32_t M,
                        int32_t E, int32_t topk, int32_t H, int32_t I, const void* out, const int32_t* topk_ids_out,
                        const float* topk_weights_out) {
-    if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if (!known_dtype(dtype)) return MOE_ERR_UNSUPPORTED;
     moe_status st = check_router(M, E, topk);
     if (st != MOE_OK) return st;
     if (H < 1 || I < 1 || H % 128 || I % 128) return MOE_ERR_SHAPE;
-    const bool fp8 = dtype == MOE_FP8_E4M3;
-    if (fp8 && (H % 256 || I % 256)) return MOE_ERR_SHAPE;
-    if (!fp8 && (x_scale || w1_scale || w2_scale)) return MOE_ERR_UNSUPPORTED;
+    const bool fp8 = dtype == MOE_FP8_E4M3, w4 = dtype == MOE_W4A16;
+    if ((fp8 || w4) && (H % 256 || I % 256)) return MOE_ERR_SHAPE;
+    if (!fp8 && x_scale) return MOE_ERR_UNSUPPORTED;
+    if (!scaled_weights(dtype) && (w1_scale || w2_scale)) return MOE_ERR_UNSUPPORTED;
     if (M == 0) return MOE_OK;
     if (!x || !router_logits || !w1 || !w2 || !out) return MOE_ERR_NULL;
-    if (fp8 && (!x_scale || !w1_scale || !w2_scale)) return MOE_ERR_NULL;
+    if (fp8 && !x_scale) return MOE_ERR_NULL;
+    if (scaled_weights(dtype) && (!w1_scale || !w2_scale)) return MOE_ERR_NULL;
     if (misaligned(x) || misaligned(router_logits) || misaligned(w1) || misaligned(w2) || misaligned(out) ||
-        misaligned(topk_ids_out) || misaligned(topk_weights_out))
+        misaligned(topk_ids_out) || misaligned(topk_weights_out) || misaligned(w1_scale) || misaligned(w2_scale))
         return MOE_ERR_ALIGNMENT;
     return MOE_OK;
 }
@@ -251,13 +258,14 @@ moe_status run_fused(moe_dtype dtype, const void* x, const float* x_scale, const
     int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;
     float* wts = topk_weights_out ? topk_weights_out : L.wts;
     float* logits = const_cast<float*>(router_logits);
+    const moe_dtype xdt = dtype == MOE_W4A16 ? MOE_BF16 : dtype;  // the activations' storage
     if (router_w && router_route_align_fits(M, E, H)) {
         // router scores, top-k and alignment in one launch
-        if (launch_router_route_align(dtype, x, x_scale, router_w, H, logits, M, E, topk, renormalize, ids, wts,
+        if (launch_router_route_align(xdt, x, x_scale, router_w, H, logits, M, E, topk, renormalize, ids, wts,
                                       L.block_m, L.cap, L.al, fp8 ? L.amax : nullptr, s) != hipSuccess)
             return MOE_ERR_HIP;
     } else {
-        if (router_w && launch_router_logits(dtype, x, x_scale, router_w, M, E, H, logits, s) != hipSuccess)
+        if (router_w && launch_router_logits(xdt, x, x_scale, router_w, M, E, H, logits, s) != hipSuccess)
             return MOE_ERR_HIP;
         if (route_align_fits(M)) {
             if (launch_route_align(logits, M, E, topk, renormalize, ids, wts, L.block_m, L.cap, L.al,

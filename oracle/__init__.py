@@ -23,8 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 
-OR_F32, OR_BF16, OR_FP8 = 0, 1, 2
-_DT = {"f32": OR_F32, "bf16": OR_BF16, "fp8": OR_FP8}
+OR_F32, OR_BF16, OR_FP8, OR_W4A16 = 0, 1, 2, 3
+_DT = {"f32": OR_F32, "bf16": OR_BF16, "fp8": OR_FP8, "w4a16": OR_W4A16}
 
 
 def build(force: bool = False) -> str:
@@ -57,6 +57,7 @@ def lib():
             "oracle_bf16_decode": (dbl, [ctypes.c_uint16]),
             "oracle_e4m3_decode": (dbl, [ctypes.c_uint8]),
             "oracle_e4m3_encode": (ctypes.c_uint8, [dbl]),
+            "oracle_int4_weight": (dbl, [P, P, i64, i64, i64, i64]),
             "oracle_num_threads": (i32, []),
             "oracle_route": (i32, [P, i64, i32, i32, i32, P, P]),
             "oracle_align_capacity": (i64, [i64, i32, i32, i32]),
@@ -215,12 +216,21 @@ def moe_layer(dtype, x, x_scale, logits, w1, w1_scale, w2, w2_scale, topk, renor
     return out
 
 
+def int4_weight(codes, gscale, n, k):
+    """W[n][k] of one expert's packed int4 matrix codes [N][K/2] with group scales [K/128][N]."""
+    cn = np.ascontiguousarray(_np(codes), np.uint8)
+    gs = np.ascontiguousarray(_np(gscale), np.float32)
+    N, K = cn.shape[0], cn.shape[1] * 2
+    return lib().oracle_int4_weight(_ptr(cn), _ptr(gs), N, K, n, k)
+
+
 def pairs_gate_up(dtype, x, x_scale, ids, w1, w1_scale, pairs):
     """act rows (float64 [n, I]) for the listed pairs p (token p//k, expert ids.flat[p])."""
     xn, w1n = _np(x), _np(w1)
     idn = np.ascontiguousarray(_np(ids), np.int32)
     M, k = idn.shape
-    E, twoI, H = w1n.shape
+    E, twoI = w1n.shape[:2]
+    H = xn.shape[1]
     pr = np.ascontiguousarray(pairs, np.int64)
     act = np.empty((len(pr), twoI // 2), np.float64)
     _check(lib().oracle_pairs_gate_up(_DT[dtype], _ptr(xn), _ptr(_f32(x_scale)), _ptr(idn), M, k,
@@ -235,7 +245,8 @@ def pairs_down(dtype, act, ids, w2, w2_scale, pairs, act_amax_value=0.0):
     adt = OR_BF16 if (isinstance(act, torch.Tensor) and act.dtype == torch.bfloat16) else OR_F32
     an, w2n = _np(act), _np(w2)
     idn = np.ascontiguousarray(_np(ids), np.int32).reshape(-1)
-    E, H, I = w2n.shape
+    E, H = w2n.shape[:2]
+    I = an.shape[1]
     pr = np.ascontiguousarray(pairs, np.int64)
     y = np.empty((len(pr), H), np.float64)
     _check(lib().oracle_pairs_down(_DT[dtype], adt, _ptr(an), float(act_amax_value), _ptr(idn),

@@ -46,7 +46,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_W4A16 = 3 };
 enum { OR_OK = 0, OR_EARG = 1, OR_ENONFINITE = 2, OR_ENOMEM = 3 };
 
 /* ---------------------------------------------------------------- codecs */
@@ -115,7 +115,54 @@ static double elem(int dtype, const void* base, int64_t i) {
     }
 }
 
-static size_t elem_bytes(int dtype) { return dtype == OR_F32 ? 4 : dtype == OR_BF16 ? 2 : 1; }
+/* Bytes of an activation element (the W4A16 layer's activations are bfloat16). */
+static size_t elem_bytes(int dtype) { return dtype == OR_F32 ? 4 : (dtype == OR_BF16 || dtype == OR_W4A16) ? 2 : 1; }
+
+/* Storage dtype of the activations. */
+static int x_dtype_of(int dtype) { return dtype == OR_W4A16 ? OR_BF16 : dtype; }
+
+/* ---------------------------------------------------- int4 weights (W4A16)
+ *
+ * Weight-only 4-bit storage of a weight matrix W[N][K] (K contiguous), the
+ * "INT4 weight quantisation" of the FusedMoE vs MegaMoE post, section 6.2
+ * (the pages fix no format; this one is symmetric round-to-nearest with one
+ * float32 scale per 128 consecutive k of a row):
+ *  - value W[n][k] = (u - 8) * scale[k / 128][n], u in [0, 15] (u = 8 + q,
+ *    q in [-7, 7] for a round-to-nearest code with scale = amax / 7);
+ *  - the codes of 8 consecutive k (k0 = a multiple of 8) fill one 32-bit
+ *    little-endian word: k0 + 2i at bits 4i..4i+3, k0 + 2i + 1 at bits
+ *    16 + 4i..16 + 4i + 3 (i = 0..3); rows are K/2 bytes, one after another;
+ *  - scales are group-major: scale[g][n] for the 128-wide group g.
+ * One expert's matrix is N*K/2 bytes of codes and (K/128)*N scales. */
+double oracle_int4_weight(const uint8_t* codes, const float* gscale, int64_t N, int64_t K, int64_t n, int64_t k) {
+    const uint8_t* p = codes + ((size_t)n * K + (size_t)(k & ~(int64_t)7)) / 2;
+    const uint32_t word = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+    const int i = (int)((k & 7) >> 1);
+    const int shift = (k & 1) ? 16 + 4 * i : 4 * i;
+    const int u = (int)((word >> shift) & 15u);
+    return (double)(u - 8) * (double)gscale[(size_t)(k / 128) * N + n];
+}
+
+/* Expert e's weight matrix (rows x K) and its scales: a byte pointer and
+ * either one scalar scale (fp8) or the group scales (W4A16). */
+static const void* wexp(int dtype, const void* w, int e, int64_t rows, int64_t K) {
+    const size_t bytes = dtype == OR_W4A16 ? (size_t)rows * K / 2 : (size_t)rows * K * elem_bytes(dtype);
+    return (const char*)w + (size_t)e * bytes;
+}
+
+static const float* wgscale(int dtype, const float* s, int e, int64_t rows, int64_t K) {
+    return dtype == OR_W4A16 ? s + (size_t)e * (K / 128) * rows : NULL;
+}
+
+/* W[n][k] of an expert matrix widened (times its scale). */
+static double wval(int dtype, const void* w_e, double w_scale, const float* gs_e, int64_t N, int64_t K, int64_t n,
+                   int64_t k);
+
+static double wval(int dtype, const void* w_e, double w_scale, const float* gs_e, int64_t N, int64_t K, int64_t n,
+                   int64_t k) {
+    if (dtype == OR_W4A16) return oracle_int4_weight((const uint8_t*)w_e, gs_e, N, K, n, k);
+    return elem(dtype, w_e, n * K + k) * w_scale;
+}
 
 int oracle_num_threads(void) {
 #ifdef _OPENMP
@@ -237,26 +284,28 @@ int oracle_align(const int32_t* ids, int64_t M, int k, int E, int bm, int64_t ca
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* a[n] = silu(W1[n].x) * W1[I+n].x for one pair, x and W1 widened (times scales). */
+/* a[n] = silu(W1[n].x) * W1[I+n].x for one pair, x and W1 widened (times
+ * scales; gs1_e: the group scales of int4 weights, else NULL). */
 void oracle_gate_up(int dtype, const void* x_row, double x_scale, const void* w1_e, double w1_scale,
-                    int64_t H, int64_t I, double* a) {
+                    const float* gs1_e, int64_t H, int64_t I, double* a) {
+    const int xd = x_dtype_of(dtype);
     for (int64_t n = 0; n < I; ++n) {
         double g = 0.0, u = 0.0;
         for (int64_t h = 0; h < H; ++h) {
-            double xv = elem(dtype, x_row, h) * x_scale;
-            g += elem(dtype, w1_e, n * H + h) * w1_scale * xv;
-            u += elem(dtype, w1_e, (I + n) * H + h) * w1_scale * xv;
+            double xv = elem(xd, x_row, h) * x_scale;
+            g += wval(dtype, w1_e, w1_scale, gs1_e, 2 * I, H, n, h) * xv;
+            u += wval(dtype, w1_e, w1_scale, gs1_e, 2 * I, H, I + n, h) * xv;
         }
         a[n] = silu(g) * u;
     }
 }
 
 /* y[h] = W2[h].a for one pair. */
-void oracle_down(int dtype, const double* a, const void* w2_e, double w2_scale, int64_t H, int64_t I,
-                 double* y) {
+void oracle_down(int dtype, const double* a, const void* w2_e, double w2_scale, const float* gs2_e, int64_t H,
+                 int64_t I, double* y) {
     for (int64_t h = 0; h < H; ++h) {
         double s = 0.0;
-        for (int64_t i = 0; i < I; ++i) s += elem(dtype, w2_e, h * I + i) * w2_scale * a[i];
+        for (int64_t i = 0; i < I; ++i) s += wval(dtype, w2_e, w2_scale, gs2_e, H, I, h, i) * a[i];
         y[h] = s;
     }
 }
@@ -273,6 +322,10 @@ void oracle_quant_act(double* a, int64_t I, double amax) {
 }
 
 static double sc(const float* p, int64_t i) { return p ? (double)p[i] : 1.0; }
+
+/* The scalar scale of expert e's matrix: fp8's per-expert scale, 1 otherwise
+ * (int4 weights carry group scales instead). */
+static double wsc(int dtype, const float* p, int e) { return dtype == OR_W4A16 ? 1.0 : sc(p, e); }
 
 /* Largest |a| over every (token, slot) pair of the batch: the dynamic
  * per-tensor statistic of the fp8 intermediate. */
@@ -300,8 +353,8 @@ int oracle_act_amax(int dtype, const void* x, const float* x_scale, const float*
             }
             for (int j = 0; j < k; ++j) {
                 int e = ids[j];
-                oracle_gate_up(dtype, (const char*)x + (size_t)t * H * eb, sc(x_scale, 0),
-                               (const char*)w1 + (size_t)e * 2 * I * H * eb, sc(w1_scale, e), H, I, a);
+                oracle_gate_up(dtype, (const char*)x + (size_t)t * H * eb, sc(x_scale, 0), wexp(dtype, w1, e, 2 * I, H),
+                               wsc(dtype, w1_scale, e), wgscale(dtype, w1_scale, e, 2 * I, H), H, I, a);
                 for (int64_t n = 0; n < I; ++n)
                     if (fabs(a[n]) > local) local = fabs(a[n]);
             }
@@ -342,8 +395,8 @@ int oracle_act_amax_per_token(int dtype, const void* x, const float* x_scale, co
             }
             for (int j = 0; j < k; ++j) {
                 int e = ids[j];
-                oracle_gate_up(dtype, (const char*)x + (size_t)t * H * eb, sc(x_scale, 0),
-                               (const char*)w1 + (size_t)e * 2 * I * H * eb, sc(w1_scale, e), H, I, a);
+                oracle_gate_up(dtype, (const char*)x + (size_t)t * H * eb, sc(x_scale, 0), wexp(dtype, w1, e, 2 * I, H),
+                               wsc(dtype, w1_scale, e), wgscale(dtype, w1_scale, e, 2 * I, H), H, I, a);
                 for (int64_t n = 0; n < I; ++n)
                     if (fabs(a[n]) > local) local = fabs(a[n]);
             }
@@ -386,10 +439,11 @@ int oracle_moe(int dtype, const void* x, const float* x_scale, const float* logi
             }
             for (int j = 0; j < k; ++j) {
                 int e = ids[j];
-                oracle_gate_up(dtype, (const char*)x + (size_t)t * H * eb, sc(x_scale, 0),
-                               (const char*)w1 + (size_t)e * 2 * I * H * eb, sc(w1_scale, e), H, I, a);
+                oracle_gate_up(dtype, (const char*)x + (size_t)t * H * eb, sc(x_scale, 0), wexp(dtype, w1, e, 2 * I, H),
+                               wsc(dtype, w1_scale, e), wgscale(dtype, w1_scale, e, 2 * I, H), H, I, a);
                 if (dtype == OR_FP8) oracle_quant_act(a, I, act_amax);
-                oracle_down(dtype, a, (const char*)w2 + (size_t)e * H * I * eb, sc(w2_scale, e), H, I, y);
+                oracle_down(dtype, a, wexp(dtype, w2, e, H, I), wsc(dtype, w2_scale, e), wgscale(dtype, w2_scale, e, H, I), H,
+                            I, y);
                 for (int64_t h = 0; h < H; ++h) o[h] += w[j] * y[h];
             }
         }
@@ -410,8 +464,8 @@ int oracle_pairs_gate_up(int dtype, const void* x, const float* x_scale, const i
     for (int64_t i = 0; i < n_pairs; ++i) {
         int64_t p = pairs[i];
         int e = ids[p];
-        oracle_gate_up(dtype, (const char*)x + (size_t)(p / k) * H * eb, sc(x_scale, 0),
-                       (const char*)w1 + (size_t)e * 2 * I * H * eb, sc(w1_scale, e), H, I, act + i * I);
+        oracle_gate_up(dtype, (const char*)x + (size_t)(p / k) * H * eb, sc(x_scale, 0), wexp(dtype, w1, e, 2 * I, H),
+                       wsc(dtype, w1_scale, e), wgscale(dtype, w1_scale, e, 2 * I, H), H, I, act + i * I);
     }
     return OR_OK;
 }
@@ -421,7 +475,7 @@ int oracle_pairs_gate_up(int dtype, const void* x, const float* x_scale, const i
 int oracle_pairs_down(int dtype, int act_dtype, const void* act, double act_amax, const int32_t* ids,
                       int64_t P, const void* w2, const float* w2_scale, int E, int64_t H, int64_t I,
                       const int64_t* pairs, int64_t n_pairs, double* y) {
-    size_t eb = elem_bytes(dtype), ab = elem_bytes(act_dtype);
+    size_t ab = elem_bytes(act_dtype);
     for (int64_t i = 0; i < n_pairs; ++i)
         if (pairs[i] < 0 || pairs[i] >= P || ids[pairs[i]] < 0 || ids[pairs[i]] >= E) return OR_EARG;
     int err = 0;
@@ -436,7 +490,8 @@ int oracle_pairs_down(int dtype, int act_dtype, const void* act, double act_amax
             int e = ids[p];
             for (int64_t n = 0; n < I; ++n) a[n] = elem(act_dtype, (const char*)act + (size_t)p * I * ab, n);
             if (dtype == OR_FP8) oracle_quant_act(a, I, act_amax);
-            oracle_down(dtype, a, (const char*)w2 + (size_t)e * H * I * eb, sc(w2_scale, e), H, I, y + i * H);
+            oracle_down(dtype, a, wexp(dtype, w2, e, H, I), wsc(dtype, w2_scale, e), wgscale(dtype, w2_scale, e, H, I),
+                        H, I, y + i * H);
         }
         free(a);
     }

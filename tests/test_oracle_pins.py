@@ -390,3 +390,59 @@ def test_router_logits_vs_numpy_matmul():
     wg1 = np.zeros((E, H), np.float32)
     wg1[3, 17] = 1.0
     assert np.array_equal(oracle.router_logits("f32", x, None, wg1)[:, 3], x[:, 17].astype(np.float64))
+
+
+# ------------------------------------------------- int4 weights (W4A16)
+
+def _unpack_int4(codes, gscale):
+    """Independent decoder of the packed int4 layout: the 4 bytes covering 8
+    consecutive k hold (k0, k0+2), (k0+4, k0+6), (k0+1, k0+3), (k0+5, k0+7)
+    as (low, high) nibbles; value = (u - 8) * scale[k // 128][n]."""
+    c = np.asarray(codes, np.uint8)
+    N, K = c.shape[0], c.shape[1] * 2
+    b = c.reshape(N, K // 8, 4)
+    u = np.empty((N, K // 8, 8), np.int64)
+    u[..., 0], u[..., 2] = b[..., 0] & 15, b[..., 0] >> 4
+    u[..., 4], u[..., 6] = b[..., 1] & 15, b[..., 1] >> 4
+    u[..., 1], u[..., 3] = b[..., 2] & 15, b[..., 2] >> 4
+    u[..., 5], u[..., 7] = b[..., 3] & 15, b[..., 3] >> 4
+    s = np.asarray(gscale, np.float64).T  # [N][K/128]
+    return (u.reshape(N, K) - 8) * np.repeat(s, 128, axis=1)
+
+
+def test_int4_packing_round_trip_and_error_bound():
+    """The generator's codes decode (independent unpacker and the oracle's
+    element accessor agree) to within half a scale step of the float32 input,
+    and a group's largest |value| is exactly 7 steps."""
+    from workloads import quant_int4_groups
+    rng = np.random.default_rng(51)
+    v = torch.from_numpy((rng.standard_normal((6, 384)) * 0.02).astype(np.float32))
+    v[2, 128:256] = 0.0  # an all-zero group: scale 1, codes 8
+    codes, gs = quant_int4_groups(v)
+    dq = _unpack_int4(codes.numpy(), gs.numpy())
+    step = np.repeat(gs.numpy().T.astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(dq - v.numpy()) <= 0.5 * step * (1 + 1e-6))
+    assert np.all(dq[2, 128:256] == 0.0) and gs[1, 2] == 1.0
+    g = np.abs(dq).reshape(6, 3, 128).max(axis=2)
+    assert np.allclose(g[g > 0] / gs.numpy().T[g > 0], 7.0)
+    for n, k in [(0, 0), (0, 1), (1, 7), (3, 8), (5, 383), (4, 200), (2, 130)]:
+        assert oracle.int4_weight(codes, gs, n, k) == dq[n, k]
+
+
+def test_w4a16_layer_matches_dense_masked_brute_force():
+    """The W4A16 layer (bf16 activations, int4 weights) against every expert
+    on every token with the independently dequantised weights."""
+    from workloads import quant_int4_groups
+    rng = np.random.default_rng(52)
+    M, E, k, H, I = 9, 5, 2, 256, 128
+    x = torch.from_numpy(rng.standard_normal((M, H)).astype(np.float32)).to(torch.bfloat16)
+    lg = rng.standard_normal((M, E)).astype(np.float32)
+    c1, s1, c2, s2, d1, d2 = [], [], [], [], [], []
+    for e in range(E):
+        a, s = quant_int4_groups(torch.from_numpy((rng.standard_normal((2 * I, H)) * 0.05).astype(np.float32)))
+        c1.append(a), s1.append(s), d1.append(_unpack_int4(a.numpy(), s.numpy()))
+        a, s = quant_int4_groups(torch.from_numpy((rng.standard_normal((H, I)) * 0.05).astype(np.float32)))
+        c2.append(a), s2.append(s), d2.append(_unpack_int4(a.numpy(), s.numpy()))
+    out = oracle.moe_layer("w4a16", x, None, lg, torch.stack(c1), torch.stack(s1), torch.stack(c2), torch.stack(s2), k)
+    ref = dense_masked(x.double().numpy(), np.stack(d1), np.stack(d2), lg, k)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())

@@ -14,4 +14,5 @@ from .gen import (  # noqa: F401
     layer_weights,
     normal_bf16,
     normal_f32,
+    quant_int4_groups,
 )

@@ -146,6 +146,26 @@ def _quant_e4m3_per_tensor(v: torch.Tensor):
     return q, torch.tensor([float(s)], dtype=torch.float32, device=v.device)
 
 
+def quant_int4_groups(v: torch.Tensor):
+    """Weight-only int4 storage of a float32 matrix v [N][K] (K a multiple of
+    128): per row and 128-wide group of k, scale = amax / 7 (float32; 1 for an
+    all-zero group) and code u = 8 + round-half-even(v / scale) clamped to
+    [1, 15].  Returns (codes uint8 [N][K/2], scales float32 [K/128][N]) in the
+    library's packing: the codes of 8 consecutive k fill one little-endian
+    32-bit word, k0+2i at bits 4i and k0+2i+1 at bits 16+4i."""
+    N, K = v.shape
+    g = v.reshape(N, K // 128, 128)
+    amax = g.abs().amax(dim=2)
+    s = torch.where(amax > 0, amax / 7.0, torch.ones_like(amax))
+    u = (torch.round(g / s[:, :, None]).clamp(-7, 7) + 8).to(torch.uint8).reshape(N, K // 8, 8)
+    b0 = u[..., 0] | (u[..., 2] << 4)
+    b1 = u[..., 4] | (u[..., 6] << 4)
+    b2 = u[..., 1] | (u[..., 3] << 4)
+    b3 = u[..., 5] | (u[..., 7] << 4)
+    codes = torch.stack([b0, b1, b2, b3], dim=2).reshape(N, K // 2)
+    return codes, s.t().contiguous()
+
+
 @dataclass(frozen=True)
 class LayerConfig:
     name: str
@@ -153,7 +173,7 @@ class LayerConfig:
     topk: int
     H: int
     I: int
-    dtype: str  # "f32" | "bf16" | "fp8"
+    dtype: str  # "f32" | "bf16" | "fp8" | "w4a16" (int4 weights, bf16 activations)
     Ms: tuple
     router: str  # "x_wg" | "normal" | "zipf"
     weight_std: float = 0.02
@@ -174,6 +194,10 @@ CONFIGS = {
                     desc="fine-grained 128-expert top-8 layer, bf16"),
         LayerConfig("fp8_e4m3", 64, 8, 4096, 8192, "fp8", (1, 32, 512), "normal",
                     desc="per-tensor-scaled OCP e4m3 layer, bf16 output"),
+        LayerConfig("mixtral_decode_w4a16", 8, 2, 4096, 14336, "w4a16", (1, 8, 32, 64), "normal",
+                    desc="Mixtral-8x7B-shaped layer, weight-only int4 (128-wide groups), bf16 activations"),
+        LayerConfig("finegrained_w4a16", 128, 8, 2048, 768, "w4a16", (1, 16), "normal",
+                    desc="fine-grained 128-expert top-8 layer, weight-only int4, bf16 activations"),
     ]
 }
 
@@ -188,6 +212,19 @@ def layer_weights(cfg: LayerConfig, device, seed: int = 0, experts=None) -> dict
     E, H, I = cfg.E, cfg.H, cfg.I
     n1, n2 = 2 * I * H, H * I
     sel = range(E) if experts is None else experts
+    if cfg.dtype == "w4a16":
+        # the bf16 layer's float32 draws, stored as int4 codes and group scales
+        w1 = torch.full((E, 2 * I, H // 2), 0x88, dtype=torch.uint8, device=device)
+        w2 = torch.full((E, H, I // 2), 0x88, dtype=torch.uint8, device=device)
+        s1 = torch.ones((E, H // 128, 2 * I), dtype=torch.float32, device=device)
+        s2 = torch.ones((E, I // 128, H), dtype=torch.float32, device=device)
+        for e in sel:
+            v = normal_f32(seed, S_W1, (2 * I, H), cfg.weight_std, device, offset=e * n1)
+            w1[e], s1[e] = quant_int4_groups(v)
+            v = normal_f32(seed, S_W2, (H, I), cfg.weight_std, device, offset=e * n2)
+            w2[e], s2[e] = quant_int4_groups(v)
+            del v
+        return {"w1": w1, "w2": w2, "w1_scale": s1, "w2_scale": s2}
     if cfg.dtype == "fp8":
         w1 = torch.zeros((E, 2 * I, H), dtype=torch.float8_e4m3fn, device=device)
         w2 = torch.zeros((E, H, I), dtype=torch.float8_e4m3fn, device=device)
@@ -232,7 +269,7 @@ def layer_batch(cfg: LayerConfig, M: int, device, seed: int = 0) -> dict:
         else:
             out["x"] = xf.to(torch.float8_e4m3fn)
             out["x_scale"] = torch.ones(1, dtype=torch.float32, device=device)
-    elif cfg.dtype == "bf16":
+    elif cfg.dtype in ("bf16", "w4a16"):
         out["x"], out["x_scale"] = normal_bf16(seed, S_X, (M, H), 1.0, device), None
     else:
         out["x"], out["x_scale"] = normal_f32(seed, S_X, (M, H), 1.0, device), None
