@@ -253,6 +253,76 @@ moe_status fused_moe_noalloc(moe_dtype dtype, const void* x, const float* x_scal
 /* MOE_NOALLOC_SCRATCH_BYTES, as a call (for bindings that cannot read macros). */
 size_t fused_moe_noalloc_scratch_bytes(void);
 
+/* ---------------------------------------------------------- expert streaming
+ * The MoE inference post's second design (FusedMoE vs MegaMoE, sections
+ * 4.1-4.3): all experts' weights stay in host memory, a GPU pool of
+ * `capacity` slots holds the experts in use, missing experts are copied in
+ * (least recently used slot first) on a copy stream that can run ahead of the
+ * compute, and the layer itself is fused_moe over the slots.
+ *
+ * The weights of a set of experts, laid out as for fused_moe: experts one
+ * after another, each expert's w1, w2 (and scales) contiguous. */
+typedef struct {
+    const void* w1;        /* [n][2I][H] (MOE_W4A16: packed codes [n][2I][H/2]) */
+    const void* w2;        /* [n][H][I]  (MOE_W4A16: [n][H][I/2])               */
+    const float* w1_scale; /* fp8: [n]; MOE_W4A16: [n][H/128][2I]; else NULL    */
+    const float* w2_scale; /* fp8: [n]; MOE_W4A16: [n][I/128][H];  else NULL    */
+} moe_expert_weights;
+
+/* Opaque cache state (host bookkeeping and HIP events). */
+typedef struct moe_expert_cache moe_expert_cache;
+
+/* Creates a cache over the E experts of `host` (pinned host memory, e.g.
+ * hipHostMalloc, with n = E; it must outlive the cache) and the device slot
+ * pool `slots` (n = capacity, 16-byte aligned; the caller owns it and keeps it
+ * for the cache's life).  copy_stream: the hipStream_t (as void*) the copies
+ * run on; a stream of its own lets them overlap the compute.  The cache starts
+ * empty.  Errors: NULL pointers -> MOE_ERR_NULL; capacity outside [1, E], H
+ * or I not multiples of 128 (256 for fp8 and W4A16) -> MOE_ERR_SHAPE; E > 256,
+ * unknown dtype, scales given for an unscaled dtype -> MOE_ERR_UNSUPPORTED;
+ * misaligned slots -> MOE_ERR_ALIGNMENT; event creation -> MOE_ERR_HIP.
+ * The cache allocates host memory for its bookkeeping and HIP events; none of
+ * its calls is thread-safe. */
+moe_status moe_cache_create(moe_dtype dtype, int32_t E, int32_t H, int32_t I, int32_t capacity,
+                            moe_expert_weights host, moe_expert_weights slots, void* copy_stream,
+                            moe_expert_cache** out);
+
+/* Waits for the copies in flight and frees the cache (not the buffers). */
+moe_status moe_cache_destroy(moe_expert_cache* cache);
+
+/* Asynchronously copies the listed experts (host ids in [0, E), repeats
+ * allowed) that are not resident into free or least recently used slots, on
+ * the copy stream (the page's predicted-expert prefetch; the prediction is
+ * the caller's).  A slot is overwritten only after the last layer call that
+ * read it; later layer calls wait for these copies only if they read the
+ * slots.  More distinct experts than slots -> MOE_ERR_UNSUPPORTED; an id out
+ * of range -> MOE_ERR_SHAPE. */
+moe_status moe_cache_prefetch(moe_expert_cache* cache, const int32_t* experts, int32_t n);
+
+/* Counters since creation: distinct experts found resident by layer calls
+ * (hits), copied by layer calls (misses), copied by prefetches, and host to
+ * device bytes of all copies.  NULL outputs are skipped. */
+moe_status moe_cache_stats(const moe_expert_cache* cache, int64_t* hits, int64_t* misses, int64_t* prefetched,
+                           int64_t* h2d_bytes);
+
+/* fused_moe over the cache: routes router_logits [M][E] over all E experts
+ * on `stream`, waits for the routing on the host (the page's synchronous miss
+ * path), copies the missing experts in, and runs alignment, both GEMMs and
+ * the combine over the slots with expert ids renamed to slot ids.  out,
+ * topk_ids_out and topk_weights_out are as for fused_moe (the ids are host
+ * expert ids).  host_ids: host int32 [M*topk] (pinned for speed) the call
+ * uses for the routed ids; leave it untouched until the stream has finished
+ * the call.  workspace: fused_moe_workspace_size(dtype, M, capacity, topk, H,
+ * I) bytes, 256-byte aligned.  Errors as for fused_moe (checked against E),
+ * plus: topk > capacity, or a batch routed to more distinct experts than
+ * slots -> MOE_ERR_UNSUPPORTED (the batch was routed, nothing else ran).
+ * Layer calls of one cache form one chain: a call on another stream waits
+ * for the previous call. */
+moe_status fused_moe_cached(moe_expert_cache* cache, const void* x, const float* x_scale,
+                            const float* router_logits, int32_t M, int32_t topk, int32_t renormalize, void* out,
+                            int32_t* topk_ids_out, float* topk_weights_out, int32_t* host_ids, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_str(moe_status s);
 

@@ -19,6 +19,7 @@ import torch
 
 from ._lib import (  # noqa: F401
     MOE_ERR_SCRATCH,
+    MOE_ERR_UNSUPPORTED,
     MOE_W4A16,
     MOE_BF16,
     MOE_F32,
@@ -27,6 +28,7 @@ from ._lib import (  # noqa: F401
     MOE_GEMM_DOWN_E4M3_ACT,
     MOE_GEMM_GATE_UP_SILU,
     AlignBufs,
+    ExpertWeights,
     MoeError,
     check,
     lib,
@@ -210,3 +212,79 @@ def fused_moe_router(x, router_w, w1, w2, topk: int, renormalize: bool = True, x
                                  _p(w2_scale), M, E, topk, H, I, int(renormalize), _p(out), _p(topk_ids),
                                  _p(topk_weights), _p(workspace), workspace.numel(), _stream(x)), "fused_moe_router")
     return out, logits
+
+
+class ExpertCache:
+    """Expert streaming (the MoE inference post, FusedMoE vs MegaMoE, sections
+    4.1-4.3): the experts' weights stay in pinned host memory and a GPU pool of
+    `capacity` slots holds the ones in use.  Calling the cache runs the layer
+    (fused_moe_cached): route, copy in the missing experts (least recently
+    used slot first), then the fused layer over the slots.  prefetch() copies
+    experts ahead of a call on the cache's own copy stream.
+
+    w1, w2 (and the scales of fp8 or W4A16 weights) are the layer's weights
+    in fused_moe's layout, on the host; they are copied once into pinned
+    memory unless already pinned."""
+
+    def __init__(self, w1, w2, capacity: int, w1_scale=None, w2_scale=None, device=None, copy_stream=None):
+        self.dtype = moe_dtype(w1)
+        self.E, twoI = w1.shape[0], w1.shape[1]
+        self.I, self.H, self.capacity = twoI // 2, w2.shape[1], capacity
+        device = torch.device("cuda" if device is None else device)
+        self.device = device if device.index is not None else torch.device("cuda", torch.cuda.current_device())
+        parts = (w1, w2, w1_scale, w2_scale)
+        if any(t is not None and t.is_cuda for t in parts):
+            raise ValueError("ExpertCache takes the experts' weights on the host")
+        self.host = [None if t is None else (t.contiguous() if t.is_pinned() else t.contiguous().pin_memory())
+                     for t in parts]
+        self.slots = [None if t is None else torch.empty((capacity,) + tuple(t.shape[1:]), dtype=t.dtype,
+                                                         device=self.device) for t in parts]
+        # default priority: copies overlap compute through events, not priorities
+        self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(self.device)
+        self._host_ids = torch.empty(0, dtype=torch.int32, pin_memory=True)
+        self._ws = None
+        h = ctypes.c_void_p()
+        check(lib().moe_cache_create(self.dtype, self.E, self.H, self.I, capacity, ExpertWeights(*map(_p, self.host)),
+                                     ExpertWeights(*map(_p, self.slots)), ctypes.c_void_p(self.copy_stream.cuda_stream),
+                                     ctypes.byref(h)), "moe_cache_create")
+        self._h = h
+
+    def prefetch(self, experts) -> None:
+        ids = torch.as_tensor(list(experts), dtype=torch.int32)
+        check(lib().moe_cache_prefetch(self._h, _p(ids), ids.numel()), "moe_cache_prefetch")
+
+    def stats(self) -> dict:
+        v = [ctypes.c_int64() for _ in range(4)]
+        check(lib().moe_cache_stats(self._h, *map(ctypes.byref, v)), "moe_cache_stats")
+        return dict(zip(("hits", "misses", "prefetched", "h2d_bytes"), (x.value for x in v)))
+
+    def __call__(self, x, router_logits, topk: int, renormalize: bool = True, x_scale=None, workspace=None,
+                 out=None, topk_ids=None, topk_weights=None):
+        """The layer over the cache; returns out[M,H] as fused_moe does."""
+        M = x.shape[0]
+        if self._host_ids.numel() < M * topk:
+            # the previous call's copy from the old buffer may still be queued
+            torch.cuda.current_stream(x.device).synchronize()
+            self._host_ids = torch.empty(M * topk, dtype=torch.int32, pin_memory=True)
+        if workspace is None:
+            need = max(fused_moe_workspace_size(self.dtype, M, self.capacity, topk, self.H, self.I), 1)
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = self._ws
+        if out is None:
+            out = torch.empty((M, self.H), dtype=_INTER[self.dtype], device=x.device)
+        check(lib().fused_moe_cached(self._h, _p(x), _p(x_scale), _p(router_logits), M, topk, int(renormalize),
+                                     _p(out), _p(topk_ids), _p(topk_weights), _p(self._host_ids), _p(workspace),
+                                     workspace.numel(), _stream(x)), "fused_moe_cached")
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            check(lib().moe_cache_destroy(self._h), "moe_cache_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -18,6 +18,10 @@ class AlignBufs(ctypes.Structure):
                 ("sorted_ids", "tile_expert", "expert_counts", "expert_offsets", "active_experts", "num_active")]
 
 
+class ExpertWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "w2", "w1_scale", "w2_scale")]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -45,6 +49,12 @@ SIGNATURES = {
     "fused_moe_noalloc": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                          _I32, _P, _P, _P, _P]),
     "fused_moe_noalloc_scratch_bytes": (_SZ, []),
+    "moe_cache_create": (ctypes.c_int, [ctypes.c_int, _I32, _I32, _I32, _I32, ExpertWeights, ExpertWeights, _P,
+                                        ctypes.POINTER(_P)]),
+    "moe_cache_destroy": (ctypes.c_int, [_P]),
+    "moe_cache_prefetch": (ctypes.c_int, [_P, _P, _I32]),
+    "moe_cache_stats": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "fused_moe_cached": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 

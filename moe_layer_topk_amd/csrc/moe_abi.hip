@@ -7,11 +7,12 @@
 
 #include <mutex>
 
+#include "moe_fused.h"
 #include "moe_launch.h"
 
 using namespace moe;
 
-namespace {
+namespace moe {
 
 constexpr int64_t kMaxPairs = 1 << 24;
 
@@ -62,21 +63,6 @@ struct Carve {
     }
 };
 
-struct FusedLayout {
-    int32_t block_m;
-    int32_t ksplit;  // K split of the DOWN GEMM (partials summed by the combine)
-    int64_t cap;
-    size_t bytes;
-    int32_t* ids;
-    float* wts;
-    moe_align_bufs al;
-    void* act;
-    void* y;
-    bool q_on_load;  // fp8: the DOWN kernel quantises the float32 act on load
-    void* act_q;     // fp8 otherwise: e4m3 codes of act
-    float* ypart;
-    float* amax;
-};
 
 FusedLayout fused_layout(char* ws, moe_dtype dtype, int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I) {
     FusedLayout L;
@@ -85,6 +71,7 @@ FusedLayout fused_layout(char* ws, moe_dtype dtype, int32_t M, int32_t E, int32_
     L.cap = moe_align_capacity(M, topk, E, L.block_m);
     Carve c{ws, 0};
     L.ids = c.take<int32_t>(P);
+    L.remap = c.take<int32_t>(P);
     L.wts = c.take<float>(P);
     L.al.sorted_ids = c.take<int32_t>(L.cap);
     L.al.tile_expert = c.take<int32_t>(L.cap / L.block_m);
@@ -103,7 +90,7 @@ FusedLayout fused_layout(char* ws, moe_dtype dtype, int32_t M, int32_t E, int32_
     return L;
 }
 
-}  // namespace
+}  // namespace moe
 
 extern "C" {
 
@@ -221,7 +208,7 @@ size_t fused_moe_workspace_size(moe_dtype dtype, int32_t M, int32_t E, int32_t t
 
 }  // extern "C"
 
-namespace {
+namespace moe {
 
 // Argument checks shared by fused_moe and fused_moe_noalloc (host only).
 moe_status check_fused(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
@@ -244,6 +231,28 @@ moe_status check_fused(moe_dtype dtype, const void* x, const float* x_scale, con
         misaligned(topk_ids_out) || misaligned(topk_weights_out) || misaligned(w1_scale) || misaligned(w2_scale))
         return MOE_ERR_ALIGNMENT;
     return MOE_OK;
+}
+
+// The expert half of the layer (GATE_UP -> DOWN -> combine) once L.al holds
+// the alignment of the routed pairs over E experts (E: the experts whose
+// weights w1/w2 hold, in that order) and wts the routing weights.
+moe_status run_experts(moe_dtype dtype, const void* x, const float* x_scale, const void* w1, const float* w1_scale,
+                       const void* w2, const float* w2_scale, int32_t M, int32_t E, int32_t topk, int32_t H,
+                       int32_t I, void* out, const float* wts, const FusedLayout& L, hipStream_t s) {
+    const bool fp8 = dtype == MOE_FP8_E4M3;
+    const moe_dtype inter = dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
+    GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, x, x_scale, w1, w1_scale, L.al, M, topk, E, 2 * I, H,
+                L.block_m, L.act, fp8 ? L.amax : nullptr};
+    if (launch_grouped_gemm(g1, s) != hipSuccess) return MOE_ERR_HIP;
+    // e4m3: the down kernel quantises the float32 intermediate as it loads it,
+    // or (tile kernels) reads codes quantised once here
+    const bool codes = fp8 && !L.q_on_load;
+    if (codes && launch_quant_act(L.act, L.amax, L.act_q, (size_t)M * topk * I, s) != hipSuccess) return MOE_ERR_HIP;
+    GemmCall g2{MOE_GEMM_DOWN, dtype, codes ? L.act_q : L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E,
+                H, I, L.block_m, L.y, nullptr, L.ksplit, L.ypart, codes};
+    if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
+    if (L.ksplit > 1) return hip_status(launch_combine_partials(L.ypart, L.ksplit, wts, M, topk, H, inter, out, s));
+    return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));
 }
 
 // The launch sequence over a carved workspace (arguments already checked, M > 0).
@@ -277,20 +286,12 @@ moe_status run_fused(moe_dtype dtype, const void* x, const float* x_scale, const
                 return MOE_ERR_HIP;
         }
     }
-    const moe_dtype inter = dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
-    GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, x, x_scale, w1, w1_scale, L.al, M, topk, E, 2 * I, H,
-                L.block_m, L.act, fp8 ? L.amax : nullptr};
-    if (launch_grouped_gemm(g1, s) != hipSuccess) return MOE_ERR_HIP;
-    // e4m3: the down kernel quantises the float32 intermediate as it loads it,
-    // or (tile kernels) reads codes quantised once here
-    const bool codes = fp8 && !L.q_on_load;
-    if (codes && launch_quant_act(L.act, L.amax, L.act_q, (size_t)M * topk * I, s) != hipSuccess) return MOE_ERR_HIP;
-    GemmCall g2{MOE_GEMM_DOWN, dtype, codes ? L.act_q : L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E,
-                H, I, L.block_m, L.y, nullptr, L.ksplit, L.ypart, codes};
-    if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
-    if (L.ksplit > 1) return hip_status(launch_combine_partials(L.ypart, L.ksplit, wts, M, topk, H, inter, out, s));
-    return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));
+    return run_experts(dtype, x, x_scale, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, out, wts, L, s);
 }
+
+}  // namespace moe
+
+namespace {
 
 // ------------------------------------------------------ static scratch
 //

@@ -183,3 +183,29 @@ def test_fused_noalloc_validation(L):
     # every decode batch (up to 64 tokens) of every layer shape fits
     for dt, E, k, H, I in [(1, 8, 2, 4096, 14336), (1, 128, 8, 2048, 768), (2, 64, 8, 4096, 8192)]:
         assert L.fused_moe_workspace_size(dt, 64, E, k, H, I) <= (64 << 20)
+
+
+def test_expert_cache_validation(L):
+    """moe_cache_create rejects bad arguments before creating any HIP object;
+    the other cache calls reject a NULL cache."""
+    from moe_layer_topk_amd._lib import ExpertWeights
+    out = ctypes.c_void_p()
+    plain = ExpertWeights(FAKE, FAKE, None, None)
+    scaled = ExpertWeights(FAKE, FAKE, FAKE, FAKE)
+    create = L.moe_cache_create
+    assert create(1, 8, 256, 256, 4, plain, plain, NULL, None) == 1  # no output handle
+    assert create(1, 8, 256, 256, 9, plain, plain, NULL, ctypes.byref(out)) == 2  # capacity > E
+    assert create(1, 8, 256, 256, 0, plain, plain, NULL, ctypes.byref(out)) == 2
+    assert create(1, 8, 200, 256, 4, plain, plain, NULL, ctypes.byref(out)) == 2  # H % 128
+    assert create(2, 8, 384, 256, 4, scaled, scaled, NULL, ctypes.byref(out)) == 2  # fp8: H % 256
+    assert create(1, 300, 256, 256, 4, plain, plain, NULL, ctypes.byref(out)) == 3  # E > 256
+    assert create(7, 8, 256, 256, 4, plain, plain, NULL, ctypes.byref(out)) == 3  # unknown dtype
+    assert create(1, 8, 256, 256, 4, scaled, scaled, NULL, ctypes.byref(out)) == 3  # scales for bf16
+    assert create(2, 8, 256, 256, 4, plain, plain, NULL, ctypes.byref(out)) == 1  # fp8 without scales
+    assert create(3, 8, 256, 256, 4, scaled, ExpertWeights(ODD, FAKE, FAKE, FAKE), NULL,
+                  ctypes.byref(out)) == 5  # misaligned slots
+    assert out.value is None
+    assert L.moe_cache_prefetch(NULL, NULL, 0) == 1
+    assert L.moe_cache_stats(NULL, None, None, None, None) == 1
+    assert L.fused_moe_cached(NULL, FAKE, None, FAKE, 1, 2, 1, FAKE, None, None, FAKE, FAKE, 1 << 20, NULL) == 1
+    assert L.moe_cache_destroy(NULL) == 0
