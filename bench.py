@@ -17,7 +17,8 @@ With no workload given, the line's `value` is the Mixtral-shaped bf16 decode
 layer at 64 tokens, and `workloads` adds the two other halves of the metric:
 the 4096-token Zipf-routed prefill layer (MFMA roofline) and the 64-expert
 e4m3 layer at 32 tokens (HBM roofline); `sweep` adds the decode layer at 1, 8
-and 32 tokens for context.
+and 32 tokens for context; `streaming` times the bf16 and int4-weight
+decode layers with host-resident experts behind a 4-slot GPU cache.
 
 Prints one JSON line.
 """
@@ -44,6 +45,10 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s & prefill MFMA TFLOP/s as % of pea
 MAIN = ("mixtral_decode_bf16", 64)
 EXTRA = (("mixtral_prefill_bf16", 4096), ("fp8_e4m3", 32), ("mixtral_decode_w4a16", 64))
 MAIN_SWEEP = (1, 8, 32)
+# expert streaming: the layers above behind a 4-slot GPU cache, 32 one-token
+# decode steps with Zipf(1.1)-skewed routing
+STREAM_CAPACITY, STREAM_STEPS = 4, 32
+STREAMED = ("mixtral_decode_bf16", "mixtral_decode_w4a16")
 
 
 def parse():
@@ -55,6 +60,7 @@ def parse():
     ap.add_argument("--M", type=int, default=None, help="tokens per batch for --workload (default: its largest)")
     ap.add_argument("--sweep", default=None, help="extra batch sizes of the main workload, e.g. 1,8,32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream", action="store_true", help="with --workload: also time it behind the expert cache")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device-to-device copy of MB MiB three times (counter calibration)")
     ap.add_argument("--traffic", default=None, metavar="DIR",
@@ -389,6 +395,75 @@ def cpu_baseline(cfg, w, M, budget_s):
             "sample": f"{cfg.name}: {what}, {passes} pass(es), {total:.2f} s"}
 
 
+def measure_streaming(moe, torch, cfg, w, dev, capacity=STREAM_CAPACITY, nsteps=STREAM_STEPS, warm=6):
+    """Expert streaming (host-resident experts, `capacity` GPU slots): one-token
+    decode steps over Zipf-routed batches, timed end to end (each step waits
+    for its routing on the host), once with copies on demand only and once
+    with the next step's routed experts prefetched while the current step
+    computes (the routed set known ahead: a perfect predictor, the upper
+    bound of prediction).  The resident layer runs the same batches."""
+    from dataclasses import replace
+
+    from workloads import layer_batch
+    zc = replace(cfg, router="zipf")
+    n = warm + nsteps
+    batches = [layer_batch(zc, 1, dev, seed=1000 + t) for t in range(n)]
+    routed = [moe.moe_route(b["logits"], zc.topk)[0].cpu().ravel().tolist() for b in batches]
+    host = {k: (None if v is None else v.cpu().pin_memory()) for k, v in w.items()}  # pinned once, used in place
+
+    def timed(step):
+        for t in range(warm):
+            step(t)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(warm, n):
+            step(t)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / nsteps
+
+    res = {"workload": zc.name, "M": 1, "capacity": capacity, "E": zc.E, "topk": zc.topk, "steps": nsteps,
+           "routing": f"Zipf({zc.zipf_s})", "dtype": DTYPE_NAME[zc.dtype]}
+    res["resident_ms_per_step"] = timed(lambda t: moe.fused_moe(batches[t]["x"], batches[t]["logits"], w["w1"],
+                                                                w["w2"], zc.topk, w1_scale=w["w1_scale"],
+                                                                w2_scale=w["w2_scale"]))
+    for name, pre in (("on_demand", False), ("prefetch_next", True)):
+        cache = moe.ExpertCache(host["w1"], host["w2"], capacity, w1_scale=host["w1_scale"],
+                                w2_scale=host["w2_scale"], device=dev)
+        marks = {}
+
+        def step(t):
+            if t == warm:
+                marks["s0"] = cache.stats()
+            cache(batches[t]["x"], batches[t]["logits"], zc.topk)
+            if pre and t + 1 < n:
+                cache.prefetch(routed[t + 1])
+
+        ms = timed(step)
+        s1 = cache.stats()
+        d = {k: s1[k] - marks["s0"][k] for k in s1}
+        cache.close()
+        res[name] = {"ms_per_step": ms, "tokens_per_s": 1e3 / ms, "misses_per_step": d["misses"] / nsteps,
+                     "prefetched_per_step": d["prefetched"] / nsteps,
+                     "hit_rate": d["hits"] / max(d["hits"] + d["misses"], 1),
+                     "h2d_GBs": d["h2d_bytes"] / (ms * 1e-3 * nsteps) / 1e9}
+    # the host link: one expert's bytes from pinned memory, timed with events
+    eb = sum(v[0].numel() * v.element_size() for k, v in host.items() if v is not None)
+    src = torch.empty(eb, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(eb, dtype=torch.uint8, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src, non_blocking=True)
+    a.record()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    res["expert_MB"] = eb / 1e6
+    res["host_link_GBs"] = 3 * eb / (a.elapsed_time(b) * 1e-3) / 1e9
+    for name in ("on_demand", "prefetch_next"):
+        res[name]["link_frac"] = res[name]["h2d_GBs"] / res["host_link_GBs"]
+    return res
+
+
 def line_entry(cfg, res, cpu):
     keys = ("ms_per_step", "tokens_per_s", "roofline_frac", "layer_hbm_frac", "layer_mfma_frac", "cold_ms_per_step",
             "cold_p10_p90_ms", "cold_roofline_frac", "graph_ms_per_step", "staged_ms_per_step", "kernel_us",
@@ -468,6 +543,19 @@ def main():
             r = measure(moe, torch, np, main_cfg, w, m, args.steps, args.warmup, dev)
             sweep.append(line_entry(main_cfg, r, None))
             print(f"[bench] {main_cfg.name} M={m}: {r['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
+    streaming = []
+
+    def stream(cfg, wx):
+        if args.workload and not args.stream:
+            return
+        if cfg.name in STREAMED:
+            r = measure_streaming(moe, torch, cfg, wx, dev)
+            streaming.append(r)
+            print(f"[bench] {cfg.name} streamed through {r['capacity']} slots: on demand "
+                  f"{r['on_demand']['ms_per_step']:.3f} ms, prefetch {r['prefetch_next']['ms_per_step']:.3f} ms, "
+                  f"resident {r['resident_ms_per_step']:.3f} ms per step", file=sys.stderr, flush=True)
+
+    stream(main_cfg, w)
     lines = []
     for cfg, m in extra:
         wx = weights_for(cfg)
@@ -475,6 +563,7 @@ def main():
         print(f"[bench] {cfg.name} M={m}: {r['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
         cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, wx, m, 4.0)
         lines.append(line_entry(cfg, r, cpu))
+        stream(cfg, wx)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -504,6 +593,7 @@ def main():
                                               "active_experts")},
         "workloads": lines,
         "sweep": sweep,
+        "streaming": streaming,
     }
     print(json.dumps(line), flush=True)
 
