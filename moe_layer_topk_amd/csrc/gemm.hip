@@ -1340,6 +1340,287 @@ static hipError_t launch_decode_ring(const GemmArgs& a, int nslots, hipStream_t 
     return hipGetLastError();
 }
 
+// -------------------------------- decode DOWN with the combine (few tokens)
+//
+// The kernel writes the final token-ordered rows itself (FusedMoE vs MegaMoE
+// post, section 3.1 step 4), so y never goes to memory and the separate
+// combine launch disappears.  Work split: blockIdx.x owns RB output columns
+// of H and runs every active expert's K steps over those weight rows; a
+// pair's y therefore stays inside one workgroup, and the combine over a
+// token's k pairs needs no other workgroup.  With RB = 16 (8) rows per
+// workgroup the grid has H/16 (H/8) workgroups, 256 for the layer shapes
+// here, as many as the per-expert decode grid it replaces.
+//
+// Unit u is an 8-row token tile of one expert (normally the expert's only
+// one); a unit has nks steps of 128 bytes of every row, brought in through
+// wavefront-private LDS rings as in the per-expert ring kernel.  With few
+// units the four waves take each unit's steps round robin (step ks to wave
+// ks mod 4) and meet at a barrier per unit, where wave u mod 4 adds the four
+// partial sums in wave order; with many, each wave runs whole units and keeps
+// the sums of the four residues ks mod 4 apart, adding them in the same
+// order.  Both are the per-expert kernel's products and sums in its order
+// (same lane layout, nks a multiple of 4), so y has the same bits; y is
+// rounded to bf16 into an LDS row per pair and the closing combine runs
+// fmaf over j ascending from 0, as the combine kernel does.
+
+static int decode_token_tiles(int M, int topk, int E);
+
+constexpr int kDcMaxPairs = 512;   // y rows kept in LDS
+constexpr int kDcMaxUnits = 320;   // >= 256 experts + 512 pairs / 8
+constexpr int kDcTok = 8;          // token rows per unit
+
+template <int RB, int KD>
+struct DcLayout {
+    static constexpr int WInstr = RB * kRingSB / 1024;       // weight copies per step
+    static constexpr int TInstr = kDcTok * kRingSB / 1024;   // token copies per step
+    static constexpr int Instr = WInstr + TInstr;
+    static constexpr int TokOff = RB * kRingSB;
+    static constexpr int Stage = (RB + kDcTok) * kRingSB;
+    static constexpr int Ring = 4 * KD * Stage;
+    static constexpr int RedOff = Ring;                              // [2][4 waves][64] f32x4
+    static constexpr int YOff = RedOff + 2 * 4 * 64 * 16;            // [kDcMaxPairs][RB] bf16
+    static constexpr int UnitOff = YOff + kDcMaxPairs * RB * 2;      // [kDcMaxUnits] int4 {e, rows, first sorted row}
+    static constexpr int PidOff = UnitOff + kDcMaxUnits * 16;        // [kDcMaxUnits][kDcTok] pair ids
+    static constexpr int Lds = PidOff + kDcMaxUnits * kDcTok * 4;
+    static_assert(Lds <= 160 * 1024, "LDS");
+    static_assert((KD - 1) * Instr < 64, "vmcnt range");
+};
+
+template <int RB, int KD>
+__global__ void __launch_bounds__(kDecThreads) gemm_down_combine_kernel(GemmArgs g, const float* __restrict__ cw,
+                                                                        uint16_t* __restrict__ out, int M) {
+    using L = DcLayout<RB, KD>;
+    extern __shared__ __attribute__((aligned(1024))) char dc_lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int drow = lane >> 3, dpc = lane & 7;
+    const int K = g.K, N = g.N;
+    const size_t rowb = (size_t)K * 2;
+    const int nks = (int)(rowb / kRingSB);  // a multiple of 4 (checked by the launcher)
+    const int n0 = blockIdx.x * RB;
+
+    int4* units = reinterpret_cast<int4*>(dc_lds + L::UnitOff);
+    int* pids = reinterpret_cast<int*>(dc_lds + L::PidOff);
+    f32x4* red = reinterpret_cast<f32x4*>(dc_lds + L::RedOff);
+    uint16_t* ybuf = reinterpret_cast<uint16_t*>(dc_lds + L::YOff);
+    int* scan = reinterpret_cast<int*>(dc_lds);  // [4] wave totals, before the rings are used
+
+    // units: thread i takes active slot i; an exclusive scan of the tiles per
+    // slot places its units (slot order, then tile order)
+    const int na = *g.num_active;
+    int e = 0, cnt = 0, tiles = 0;
+    if (tid < na) {
+        e = g.active[tid];
+        cnt = g.counts[e];
+        tiles = (cnt + kDcTok - 1) / kDcTok;
+    }
+    int incl = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) scan[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += scan[w];
+    const int U = scan[0] + scan[1] + scan[2] + scan[3];
+    __syncthreads();
+    const int first = before + incl - tiles;
+    for (int q = 0; q < tiles; ++q)
+        units[first + q] = make_int4(e, min(kDcTok, cnt - kDcTok * q), g.offsets[e] + kDcTok * q, 0);
+    __syncthreads();
+    // the tiles' pair ids (rows past a tile's count repeat its last pair)
+    for (int i = tid; i < U * kDcTok; i += kDecThreads) {
+        const int4 un = units[i / kDcTok];
+        pids[i] = g.sorted[un.z + min(i % kDcTok, un.y - 1)];
+    }
+    __syncthreads();
+
+    // Two orders of the same sums.  Few units (split): the four waves take
+    // each unit's K steps round robin and meet at a barrier per unit.  Many
+    // units: wave w runs units w, w+4, ... alone, keeping the partial sums of
+    // the four K residues apart (acc[r] = what wave r holds in the split
+    // order) and adding them in the same order, with no barrier until the end.
+    const bool split = U < 8;
+    const int jpu = nks / 4;
+    const int mine = split ? U : (U > wave ? (U - wave + 3) / 4 : 0);
+    const int nsteps = split ? U * jpu : mine * nks;
+    auto unit_of = [&](int j, int& u, int& ks) {
+        if (split) {
+            u = j / jpu;
+            ks = wave + 4 * (j - u * jpu);
+        } else {
+            const int i = j / nks;
+            u = wave + 4 * i;
+            ks = j - i * nks;
+        }
+    };
+
+    size_t woff[L::WInstr];
+#pragma unroll
+    for (int i = 0; i < L::WInstr; ++i) {
+        const int ri = 8 * i + drow;
+        woff[i] = (size_t)(n0 + ri) * rowb + ring_swz(dpc, ri) * 16;
+    }
+    const char* wall = reinterpret_cast<const char*>(g.w);
+    const char* aall = reinterpret_cast<const char*>(g.a);
+    char* ring = dc_lds + wave * (KD * L::Stage);
+    const unsigned ring_lds0 = lds_addr_of(ring);
+
+    auto issue = [&](int j) {
+        int u, ks;
+        unit_of(j, u, ks);
+        const int ue = units[u].x;
+        const int p = pids[u * kDcTok + drow];
+        const unsigned st = ring_lds0 + (unsigned)((j % KD) * L::Stage);
+        // this wave's earlier LDS reads of the slot (and of the tables) have completed
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const char* wsrc = wall + (size_t)ue * N * rowb + (size_t)ks * kRingSB;
+#pragma unroll
+        for (int i = 0; i < L::WInstr; ++i) lds_dma16_nt_at(wsrc + woff[i], st + i * 1024);
+        lds_dma16_at(aall + (size_t)ks * kRingSB + (size_t)p * rowb + ring_swz(dpc, drow) * 16, st + L::TokOff);
+    };
+    // one step: wait for stage j, two MFMAs into acc
+    const int ar = (RB == 16) ? lr : (lr & 7);  // weight row of this lane's MFMA row (RB 8: rows 8-15 repeat 0-7)
+    const int br = lr & 7;                      // token row (columns 8-15 repeat 0-7)
+    const int swa = (ar >> 1) & 7, swb = (br >> 1) & 7;
+    auto step = [&](int j, f32x4& acc) {
+        if (j + KD - 1 < nsteps) {
+            issue(j + KD - 1);
+            ring_wait_vm<(KD - 1) * L::Instr>();
+        } else {
+            ring_wait_vm<0>();
+        }
+        const char* st = ring + (j % KD) * L::Stage;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint4 a = *reinterpret_cast<const uint4*>(st + ar * kRingSB + (((4 * u + lg) ^ swa) << 4));
+            const uint4 b = *reinterpret_cast<const uint4*>(st + L::TokOff + br * kRingSB + (((4 * u + lg) ^ swb) << 4));
+            acc = Opnd<MOE_BF16>::mfma(a, b, acc);
+        }
+    };
+    // y of unit u (this lane's 4 rows of column lr) into the pair rows of LDS
+    auto store_y = [&](int u, const f32x4& ys) {
+        if (lr < units[u].y && (RB == 16 || lg < 2)) {
+            uint2 pk;
+            pk.x = pack_bf2(ys[0], ys[1]);
+            pk.y = pack_bf2(ys[2], ys[3]);
+            *reinterpret_cast<uint2*>(ybuf + pids[u * kDcTok + lr] * RB + 4 * lg) = pk;
+        }
+    };
+
+    // vmcnt(0) as a builtin the compiler sees: the table loads above are then
+    // complete on every path into the loop, so it adds no wait of its own
+    // there (it would drain the copies in flight every iteration)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+    for (int j = 0; j < KD - 1; ++j)
+        if (j < nsteps) issue(j);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    if (split) {
+        f32x4 acc = zero;
+        for (int j = 0; j < nsteps; ++j) {
+            step(j, acc);
+            if ((j + 1) % jpu == 0) {
+                // end of unit u: the four partial sums, added in wave order by wave u mod 4
+                const int u = j / jpu;
+                f32x4* r = red + (u & 1) * 4 * 64;
+                r[wave * 64 + lane] = acc;
+                acc = zero;
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (wave == (u & 3)) {
+                    f32x4 ys = zero;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) ys += r[w * 64 + lane];
+                    store_y(u, ys);
+                }
+            }
+        }
+    } else {
+        f32x4 acc0 = zero, acc1 = zero, acc2 = zero, acc3 = zero;
+        for (int j = 0; j < nsteps; j += 4) {  // nks, and so nsteps, is a multiple of 4
+            step(j, acc0);
+            step(j + 1, acc1);
+            step(j + 2, acc2);
+            step(j + 3, acc3);
+            if ((j + 4) % nks == 0) {
+                f32x4 ys = zero;
+                ys += acc0;
+                ys += acc1;
+                ys += acc2;
+                ys += acc3;
+                store_y(wave + 4 * (j / nks), ys);
+                acc0 = acc1 = acc2 = acc3 = zero;
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // out[t] = sum_j w[t,j] y[t*k+j], j ascending, 8 columns per thread
+    for (int i = tid; i < M * (RB / 8); i += kDecThreads) {
+        const int t = i / (RB / 8), h = 8 * (i % (RB / 8));
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < g.topk; ++j) {
+            const float wj = cw[(size_t)t * g.topk + j];
+            const uint4 v = *reinterpret_cast<const uint4*>(ybuf + (t * g.topk + j) * RB + h);
+            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                o[2 * c] = fmaf(wj, __uint_as_float(q[c] << 16), o[2 * c]);
+                o[2 * c + 1] = fmaf(wj, __uint_as_float(q[c] & 0xffff0000u), o[2 * c + 1]);
+            }
+        }
+        uint4 pk;
+        pk.x = pack_bf2(o[0], o[1]);
+        pk.y = pack_bf2(o[2], o[3]);
+        pk.z = pack_bf2(o[4], o[5]);
+        pk.w = pack_bf2(o[6], o[7]);
+        *reinterpret_cast<uint4*>(out + (size_t)t * N + n0 + h) = pk;
+    }
+}
+
+template <int RB, int KD>
+static hipError_t launch_down_combine_rb(const GemmArgs& a, const float* w, void* out, int M, hipStream_t s) {
+    using L = DcLayout<RB, KD>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_down_combine_kernel<RB, KD>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        L::Lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gemm_down_combine_kernel<RB, KD>), dim3(a.N / RB), dim3(kDecThreads), L::Lds, s, a, w,
+                       static_cast<uint16_t*>(out), M);
+    return hipGetLastError();
+}
+
+// Opt-in (MOE_DOWN_COMBINE=1): measured on MI355X it does not beat the
+// per-expert kernel plus the combine launch (Mixtral-shaped layer at 1 and 4
+// tokens: 1% and 0.5% slower; 128-expert layer at 1, 8 and 16 tokens: 4%,
+// 13% and 9% slower).  The launch it saves overlaps the previous kernel's
+// tail, while the column-block order re-reads each unit's token rows for
+// every block of 8 or 16 weight rows instead of every 64 to 256.
+bool down_combine_fits(moe_dtype dtype, int M, int topk, int E, int H, int I, int block_m) {
+    if (dtype != MOE_BF16 || M < 1 || block_m != 16) return false;
+    const char* env = getenv("MOE_DOWN_COMBINE");
+    if (!env || strcmp(env, "1") != 0) return false;
+    GemmCall probe{MOE_GEMM_DOWN, dtype, nullptr, nullptr, nullptr, nullptr, {}, M, topk, E, H, I, block_m,
+                   nullptr, nullptr};
+    if (choose_gemm_path(probe) != GemmPath::kDecode) return false;
+    // one 16-row token tile per expert expected (the per-expert kernel's one-tile case)
+    if (decode_token_tiles(M, topk, E) != 1) return false;
+    return (long)M * topk <= kDcMaxPairs && I % 256 == 0 && H % 16 == 0;
+}
+
+hipError_t launch_down_combine(const GemmCall& c, const float* topk_weights, void* out, hipStream_t s) {
+    GemmArgs a{c.a, c.a_scale, c.w, c.w_scale, c.al.sorted_ids, c.al.tile_expert, c.al.expert_counts,
+               c.al.expert_offsets, c.al.active_experts, c.al.num_active, c.topk, c.N, c.K, c.M * c.topk,
+               nullptr, nullptr, 1, nullptr, 0};
+    // 256 workgroups where H allows: 16 rows each from H = 4096 up, else 8
+    if (c.N >= 4096) return launch_down_combine_rb<16, 8>(a, topk_weights, out, c.M, s);
+    return launch_down_combine_rb<8, 12>(a, topk_weights, out, c.M, s);
+}
+
 // ------------------------------------------- decode, int4 weights (W4A16)
 //
 // Weight-only int4 (FusedMoE vs MegaMoE post, sections 6.2-6.3: INT4 weights

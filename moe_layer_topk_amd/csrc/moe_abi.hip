@@ -81,10 +81,11 @@ FusedLayout fused_layout(char* ws, moe_dtype dtype, int32_t M, int32_t E, int32_
     L.al.num_active = c.take<int32_t>(1);
     L.amax = c.take<float>(1);
     L.act = c.take<char>((size_t)P * I * act_bytes(dtype));
-    L.y = c.take<char>((size_t)P * H * inter_bytes(dtype));
+    L.dc = down_combine_fits(dtype, M, topk, E, H, I, L.block_m);
+    L.y = L.dc ? nullptr : c.take<char>((size_t)P * H * inter_bytes(dtype));
     L.q_on_load = dtype == MOE_FP8_E4M3 && fp8_down_quantises_on_load(M, topk, E, H, I, L.block_m);
     L.act_q = (dtype == MOE_FP8_E4M3 && !L.q_on_load) ? c.take<char>((size_t)P * I) : nullptr;
-    L.ksplit = down_ksplit(dtype, M, topk, E, H, I, L.block_m);
+    L.ksplit = L.dc ? 1 : down_ksplit(dtype, M, topk, E, H, I, L.block_m);
     L.ypart = L.ksplit > 1 ? c.take<float>((size_t)L.ksplit * P * H) : nullptr;
     L.bytes = c.off;
     return L;
@@ -250,6 +251,7 @@ moe_status run_experts(moe_dtype dtype, const void* x, const float* x_scale, con
     if (codes && launch_quant_act(L.act, L.amax, L.act_q, (size_t)M * topk * I, s) != hipSuccess) return MOE_ERR_HIP;
     GemmCall g2{MOE_GEMM_DOWN, dtype, codes ? L.act_q : L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E,
                 H, I, L.block_m, L.y, nullptr, L.ksplit, L.ypart, codes};
+    if (L.dc) return hip_status(launch_down_combine(g2, wts, out, s));  // y stays on chip
     if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
     if (L.ksplit > 1) return hip_status(launch_combine_partials(L.ypart, L.ksplit, wts, M, topk, H, inter, out, s));
     return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));

@@ -23,6 +23,7 @@ struct FusedLayout {
     void* act;
     void* y;
     bool q_on_load;  // fp8: the DOWN kernel quantises the float32 act on load
+    bool dc;         // the DOWN kernel also combines (no y, no combine launch)
     void* act_q;     // fp8 otherwise: e4m3 codes of act
     float* ypart;
     float* amax;

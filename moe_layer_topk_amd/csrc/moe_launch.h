@@ -65,6 +65,13 @@ int prefill_supported_block_m(int block_m);
 
 hipError_t launch_grouped_gemm(const GemmCall& g, hipStream_t s);
 
+// Decode DOWN GEMM with the combine inside (bf16, about one 16-row token tile
+// per expert, at most 512 pairs, I a multiple of 256): out[M][H] directly,
+// the same bits as the per-expert DOWN kernel followed by launch_combine.
+// Used by the fused layer only with MOE_DOWN_COMBINE=1 (not faster here).
+bool down_combine_fits(moe_dtype dtype, int M, int topk, int E, int H, int I, int block_m);
+hipError_t launch_down_combine(const GemmCall& c, const float* topk_weights, void* out, hipStream_t s);
+
 // K split the fused layer uses for the DOWN GEMM (1 when the decode kernel
 // already has enough workgroups, or when the prefill kernel serves the call).
 int down_ksplit(moe_dtype dtype, int M, int topk, int E, int N, int K, int block_m);

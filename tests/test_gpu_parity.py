@@ -211,6 +211,36 @@ def test_fp8_down_quantise_on_load_equals_codes(dev, monkeypatch):
         assert rel_err(y, yref) <= TOL["fp8"]
 
 
+def test_register_kernel_four_groups_two_token_tiles(dev, monkeypatch):
+    """The register-operand decode kernel at four row groups and two token
+    tiles (128 KiB of LDS for its cross-wavefront reduction): the down GEMM of
+    a float32 layer with a short K (I = 512), and a standalone e4m3 DOWN over a
+    float32 intermediate (K = 2048), both at 12 pairs per expert on average."""
+    import moe_layer_topk_amd as moe
+    cfg = replace(CONFIGS["tiny_f32"], E=64, topk=8, H=4096, I=512, router="normal")
+    say("register kernel: f32 layer E=64 k=8 H=4096 I=512 M=96")
+    check_layer(cfg, 96, dev, tokens=range(0, 96, 7))
+    _W.clear()
+    monkeypatch.setenv("MOE_GEMM_PATH", "decode")
+    E, k, H, I, M = 64, 8, 4096, 2048, 96
+    say(f"register kernel: fp8 DOWN on float32 act E={E} k={k} H={H} I={I} M={M}")
+    cfg = replace(CONFIGS["fp8_e4m3"], E=E, topk=k, H=H, I=I, router="normal")
+    w = layer_weights(cfg, dev, seed=4)  # drawn on the GPU: 64 experts are slow to draw on the host
+    b = layer_batch(cfg, M, "cpu", seed=4)
+    rid, _ = oracle.route(b["logits"], k)
+    al = moe.moe_align(torch.from_numpy(rid).to(dev), E, 16)
+    a_in = normal_f32(seed=9, stream=S_ACT, shape=(M * k, I), std=0.3, device=dev)
+    amax = a_in.abs().max().reshape(1)
+    y, _ = moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN, a_in, w["w2"], al, M, k, a_scale=amax, w_scale=w["w2_scale"])
+    torch.cuda.synchronize()
+    pairs = np.arange(0, M * k, 13)
+    yref = oracle.pairs_down("fp8", a_in.cpu(), rid, w["w2"].cpu(), w["w2_scale"].cpu(), pairs,
+                             act_amax_value=float(amax))
+    err = rel_err(y.cpu()[torch.from_numpy(pairs)], yref)
+    say(f"  down rel err {err:.2e} over {len(pairs)} pairs")
+    assert err <= TOL["fp8"]
+
+
 def test_quant_act_codes_exhaustive_near_ties(dev):
     """moe_quant_act against the oracle's encoder on values placed at, just
     below and just above every e4m3 rounding midpoint (and the saturation
@@ -446,6 +476,43 @@ def test_fp8_scale_product_invariance_gpu(dev, M):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
     assert torch.equal(o4.float(), o1.float() * 4)
+
+
+# the decode DOWN GEMM with the combine inside (bf16, about one token tile per
+# expert): Mixtral and 128-expert shapes, a skewed batch whose first expert
+# takes 32 pairs (two token tiles in one workgroup's sequence), H = 2048 (8
+# output columns per workgroup) and H = 4096 (16)
+DOWN_COMBINE = [("mixtral_decode_bf16", {}, 1, None), ("mixtral_decode_bf16", {}, 3, None),
+                ("finegrained_bf16", {}, 1, None), ("finegrained_bf16", {}, 16, None),
+                ("finegrained_bf16", {"E": 64, "topk": 2}, 32, 0), ("finegrained_bf16", {"H": 4096, "I": 512}, 5, None)]
+
+
+@pytest.mark.parametrize("name,shape,M,skew", DOWN_COMBINE)
+def test_down_combine_bitwise_equals_separate(dev, monkeypatch, name, shape, M, skew):
+    """The fused layer's DOWN-with-combine kernel (opt-in) against the per-step
+    path (DOWN GEMM into y, then moe_combine) on the same intermediate: the
+    same bits; and the layer against the oracle."""
+    import moe_layer_topk_amd as moe
+    monkeypatch.setenv("MOE_DOWN_COMBINE", "1")
+    cfg = replace(CONFIGS[name], **shape)
+    say(f"down+combine {cfg.name} {shape} M={M} skew={skew}")
+    w, wh = weights(cfg, dev)
+    b = layer_batch(cfg, M, dev, seed=11)
+    if skew is not None:
+        b["logits"][:, skew] += 50.0  # every token's first choice
+    k, E = cfg.topk, cfg.E
+    ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((M, k), dtype=torch.float32, device=dev)
+    out = moe.fused_moe(b["x"], b["logits"], w["w1"], w["w2"], k, topk_ids=ids, topk_weights=wts)
+    al = moe.moe_align(ids, E, 16)
+    act, _ = moe.moe_grouped_gemm(moe.MOE_GEMM_GATE_UP_SILU, b["x"], w["w1"], al, M, k)
+    y, _ = moe.moe_grouped_gemm(moe.MOE_GEMM_DOWN, act, w["w2"], al, M, k)
+    ref = moe.moe_combine(y, wts, k)
+    torch.cuda.synchronize()
+    if skew is not None:
+        assert int((ids[:, 0] == skew).sum()) == M
+    assert torch.equal(out, ref), (out.float() - ref.float()).abs().max().item()
+    check_layer(cfg, M, dev, batch=b)
 
 
 def test_fused_deterministic(dev):
