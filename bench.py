@@ -281,6 +281,31 @@ def measure(moe, torch, np, cfg, w, M, steps, warmup, dev, events=True):
     res["graph_ms_per_step"] = (time.perf_counter() - t) / steps * 1e3
     del g
 
+    # the layer from the hidden states: router scores x . Wg^T on the GPU first
+    # (fused_moe_router; router weights float32 [E, H] ~ N(0, 0.02))
+    from workloads.gen import S_WG, normal_f32
+    wg = normal_f32(0, S_WG, (E, H), 0.02, dev)
+    lg = torch.empty((M, E), dtype=torch.float32, device=dev)
+
+    def routed():
+        moe.fused_moe_router(b["x"], wg, w["w1"], w["w2"], k, x_scale=b["x_scale"], w1_scale=w["w1_scale"],
+                             w2_scale=w["w2_scale"], workspace=ws, out=out, logits=lg, topk_ids=ids)
+
+    for _ in range(warmup):
+        routed()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        routed()
+    torch.cuda.synchronize()
+    rs = (time.perf_counter() - t) / steps
+    res["router_ms_per_step"] = rs * 1e3
+    # its own routing activates its own experts: roofline on those
+    ra = int(torch.unique(ids).numel())
+    res["router_active_experts"] = ra
+    res["router_roofline_frac"] = max(layer_bytes(cfg, M, ra, wb, xb, ob) / (HBM_PEAK_GBS * 1e9), fl / peak_f) / rs
+    del wg, lg
+
     # per-kernel durations through the per-step entry points (the kernels fused_moe launches, except
     # that the per-step down GEMM does not split K), HIP events around each launch on torch's stream
     block_m = fused_block_m(cfg, M)
@@ -466,7 +491,9 @@ def measure_streaming(moe, torch, cfg, w, dev, capacity=STREAM_CAPACITY, nsteps=
 
 def line_entry(cfg, res, cpu):
     keys = ("ms_per_step", "tokens_per_s", "roofline_frac", "layer_hbm_frac", "layer_mfma_frac", "cold_ms_per_step",
-            "cold_p10_p90_ms", "cold_roofline_frac", "graph_ms_per_step", "staged_ms_per_step", "kernel_us",
+            "cold_p10_p90_ms", "cold_roofline_frac", "graph_ms_per_step", "router_ms_per_step",
+            "router_active_experts", "router_roofline_frac", "staged_ms_per_step",
+            "kernel_us",
             "gate_up_GBs", "gate_up_TFLOPs", "down_GBs", "down_TFLOPs", "active_experts")
     e = {"workload": cfg.name, "M": res["M"], "dtype": DTYPE_NAME[cfg.dtype],
          "E": cfg.E, "topk": cfg.topk, "hidden": cfg.H, "intermediate": cfg.I}
@@ -589,6 +616,8 @@ def main():
         "cpu_baseline": cpu,
         "layer": {k2: main_res[k2] for k2 in ("roofline_frac", "layer_hbm_frac", "layer_mfma_frac", "cold_ms_per_step",
                                               "cold_p10_p90_ms", "cold_roofline_frac", "graph_ms_per_step",
+                                              "router_ms_per_step", "router_active_experts",
+                                              "router_roofline_frac",
                                               "kernel_us", "staged_ms_per_step", "gate_up_GBs", "down_GBs",
                                               "active_experts")},
         "workloads": lines,

@@ -167,26 +167,44 @@ __device__ __forceinline__ void router_block(const void* __restrict__ x, float s
     for (int t = 0; t < TT; ++t)
 #pragma unroll
         for (int e = 0; e < TE; ++e) acc[t][e] = 0.0f;
-#pragma unroll UH
-    for (int h0 = 4 * lane; h0 < H; h0 += 256) {
-        float4 w4[TE], x4[TT];
+    // rows past M (E) read the last row: every load is unconditional, so a
+    // chunk's loads are all issued before its first product; those sums are
+    // never stored.  Lanes past H (H an odd multiple of 128) add nothing.
+    const char* xr[TT];
+    const float* wr[TE];
 #pragma unroll
-        for (int e = 0; e < TE; ++e)
-            w4[e] = (e0 + e < E) ? *reinterpret_cast<const float4*>(wg + (size_t)(e0 + e) * H + h0)
-                                 : float4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TT; ++t) xr[t] = reinterpret_cast<const char*>(x) + (size_t)min(t0 + t, M - 1) * H * (XDT == MOE_F32 ? 4 : XDT == MOE_BF16 ? 2 : 1);
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
-            x4[t] = (t0 + t < M) ? router_x4<XDT>(x, (size_t)(t0 + t) * H + h0, sx) : float4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < TE; ++e) wr[e] = wg + (size_t)min(e0 + e, E - 1) * H;
+    const int nit = (H + 255) / 256;
+    for (int i0 = 0; i0 < nit; i0 += UH) {
+        float4 w4[UH][TE], x4[UH][TT];
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
+        for (int u = 0; u < UH; ++u) {
+            const int h = min(256 * (i0 + u) + 4 * lane, H - 4);
 #pragma unroll
-            for (int e = 0; e < TE; ++e) {
-                float a = acc[t][e];
-                a = __builtin_fmaf(x4[t].x, w4[e].x, a);
-                a = __builtin_fmaf(x4[t].y, w4[e].y, a);
-                a = __builtin_fmaf(x4[t].z, w4[e].z, a);
-                acc[t][e] = __builtin_fmaf(x4[t].w, w4[e].w, a);
-            }
+            for (int e = 0; e < TE; ++e) w4[u][e] = *reinterpret_cast<const float4*>(wr[e] + h);
+#pragma unroll
+            for (int t = 0; t < TT; ++t) x4[u][t] = router_x4<XDT>(xr[t], (size_t)h, sx);
+        }
+#pragma unroll
+        for (int u = 0; u < UH; ++u) {
+            // steps past the row (the last chunk's tail, or this lane's last
+            // step when H is an odd multiple of 128) add nothing; no branch,
+            // so the chunk's loads stay ahead of its products
+            const bool live = 256 * (i0 + u) + 4 * lane < H;
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int e = 0; e < TE; ++e) {
+                    float a = acc[t][e];
+                    a = __builtin_fmaf(x4[u][t].x, w4[u][e].x, a);
+                    a = __builtin_fmaf(x4[u][t].y, w4[u][e].y, a);
+                    a = __builtin_fmaf(x4[u][t].z, w4[u][e].z, a);
+                    a = __builtin_fmaf(x4[u][t].w, w4[u][e].w, a);
+                    acc[t][e] = live ? a : acc[t][e];
+                }
+        }
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t)
@@ -200,43 +218,46 @@ __device__ __forceinline__ void router_block(const void* __restrict__ x, float s
 }
 
 // One wavefront per block of TT tokens x TE experts, four per workgroup, no
-// LDS and no barrier (every load of a wavefront is independent of its other
-// loads, so they overlap).  The block shape only spreads the work: one
-// expert per wavefront while that makes fewer than 1024 blocks (more
-// wavefronts for few tokens), else 4 (each token row read a quarter as often).
-constexpr int kRtTT = 8;
-
-template <int XDT, int TE>
+// LDS and no barrier.  The block shape only spreads the work: for a few
+// tokens one token and one expert per wavefront (as many wavefronts as
+// scores, each a chain of H/256 steps whose loads are issued UH at a time);
+// for many, 8 tokens by 1 expert while that makes fewer than 1024 blocks,
+// else 8 by 4 (each row of x and of the router read a quarter as often).
+template <int XDT, int TT, int TE>
 __global__ void __launch_bounds__(256) router_logits_kernel(const void* __restrict__ x, const float* __restrict__ x_scale,
                                                             const float* __restrict__ wg, int M, int E, int H,
                                                             float* __restrict__ logits) {
     const int eblocks = (E + TE - 1) / TE;
     const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (blk >= ((M + kRtTT - 1) / kRtTT) * eblocks) return;
-    const int t0 = (blk / eblocks) * kRtTT, e0 = (blk % eblocks) * TE;
+    if (blk >= ((M + TT - 1) / TT) * eblocks) return;
+    const int t0 = (blk / eblocks) * TT, e0 = (blk % eblocks) * TE;
     const float sx = x_scale ? x_scale[0] : 1.0f;
-    float acc[kRtTT][TE];
-    router_block<XDT, kRtTT, TE>(x, sx, wg, M, E, H, t0, e0, acc);
+    float acc[TT][TE];
+    // loads in flight per chunk: all 16 steps of a 4096-wide row for one score
+    router_block<XDT, TT, TE, TT == 1 ? 16 : (TE == 1 ? 4 : 2)>(x, sx, wg, M, E, H, t0, e0, acc);
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int t = 0; t < kRtTT; ++t)
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
         for (int e = 0; e < TE; ++e)
             if (lane == t * TE + e && t0 + t < M && e0 + e < E) logits[(size_t)(t0 + t) * E + e0 + e] = acc[t][e];
 }
 
+template <int XDT, int TT, int TE>
+static hipError_t launch_router_tt(const void* x, const float* x_scale, const float* wg, int M, int E, int H,
+                                   float* logits, hipStream_t s) {
+    const long blocks = (long)((M + TT - 1) / TT) * ((E + TE - 1) / TE);
+    hipLaunchKernelGGL((router_logits_kernel<XDT, TT, TE>), dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0, s, x,
+                       x_scale, wg, M, E, H, logits);
+    return hipGetLastError();
+}
+
 template <int XDT>
 static hipError_t launch_router_x(const void* x, const float* x_scale, const float* wg, int M, int E, int H,
                                   float* logits, hipStream_t s) {
-    const long tblocks = (M + kRtTT - 1) / kRtTT;
-    const int te = tblocks * E < 1024 ? 1 : 4;
-    const long blocks = (long)((M + kRtTT - 1) / kRtTT) * ((E + te - 1) / te);
-    const dim3 grid((unsigned)((blocks + 3) / 4));
-    if (te == 1)
-        hipLaunchKernelGGL((router_logits_kernel<XDT, 1>), grid, dim3(256), 0, s, x, x_scale, wg, M, E, H, logits);
-    else
-        hipLaunchKernelGGL((router_logits_kernel<XDT, 4>), grid, dim3(256), 0, s, x, x_scale, wg, M, E, H, logits);
-    return hipGetLastError();
+    if ((long)M * E <= 4096) return launch_router_tt<XDT, 1, 1>(x, x_scale, wg, M, E, H, logits, s);
+    if ((long)((M + 7) / 8) * E < 1024) return launch_router_tt<XDT, 8, 1>(x, x_scale, wg, M, E, H, logits, s);
+    return launch_router_tt<XDT, 8, 4>(x, x_scale, wg, M, E, H, logits, s);
 }
 
 hipError_t launch_router_logits(moe_dtype xdt, const void* x, const float* x_scale, const float* wg, int M, int E,
