@@ -1652,8 +1652,16 @@ hipError_t launch_down_combine(const GemmCall& c, const float* topk_weights, voi
 // covers 32 k of one group (lane group lg: k = 128 g + 32 lg + 8 q + j), so
 // every group's products are accumulated apart and scaled per row.
 
+// Two codes of a word (bits 0-3 and 16-19 of w) as two bf16 words 128 + u:
+// (w & 0x000F000F) | 0x43004300 in one v_and_or_b32.
+__device__ __forceinline__ uint32_t w4_bf16x2(uint32_t w, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "v"(mask), "v"(magic));
+    return r;
+}
+
 template <int KIND, int NT, int G, int KD>
-__global__ void __launch_bounds__(kDecThreads) gemm_decode_w4_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs g) {
     constexpr int T = 4;                      // 16-row tiles per group of 64 rows
     constexpr int kWInstr = 64 * kRingSB / 1024;
     constexpr int kScaleOff = 64 * kRingSB;   // [2 groups][64 rows] float32 after the codes
@@ -1682,12 +1690,14 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_w4_kernel(GemmArgs g)
     const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 32 * G : blockIdx.x * 64 * G;
     const int grows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 : 64;  // row offset between this block's groups
     const char* wexp = reinterpret_cast<const char*>(g.w) + (size_t)e * N * rowb;
-    size_t woff[kWInstr];
+    // 32-bit offsets inside one expert's matrix (N * K / 2 bytes < 4 GiB,
+    // checked by the launcher): registers are what bounds this kernel
+    uint32_t woff[kWInstr];
 #pragma unroll
     for (int i = 0; i < kWInstr; ++i) {
         const int ri = 8 * i + drow;
         const int row = (KIND == MOE_GEMM_GATE_UP_SILU) ? ((ri < 32) ? n0 + ri : I + n0 + ri - 32) : n0 + ri;
-        woff[i] = (size_t)row * rowb + ring_swz(dpc, ri) * 16;
+        woff[i] = (uint32_t)row * (uint32_t)rowb + (uint32_t)ring_swz(dpc, ri) * 16u;
     }
     // the scale copy: lane l (mod 32) brings 4 scales of group (l / 16) of the
     // step, rows 4 (l % 16).. of the 64 (gate rows then up rows for GATE_UP),
@@ -1700,6 +1710,10 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_w4_kernel(GemmArgs g)
     const unsigned ring_lds0 = lds_addr_of(ring);
     f32x4* red = reinterpret_cast<f32x4*>(w4_lds);  // after the main loop only
     const uint4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
+    // the AND-OR constants in registers: the fused v_and_or_b32 (VOP3) takes
+    // no literal on this target
+    const uint32_t nib_mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+    const uint32_t bf_magic = __builtin_amdgcn_readfirstlane(0x43004300u);
 
     for (int pass = 0; pass < cnt; pass += NT * 16) {
         const int ntiles = min(NT, (cnt - pass + 15) / 16);
@@ -1793,19 +1807,19 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_w4_kernel(GemmArgs g)
                             *reinterpret_cast<const uint4*>(st + (16 * t + lr) * kRingSB + (((4 * kg + lg) ^ sw) << 4));
                         const f32x4 s4 = *reinterpret_cast<const f32x4*>(sc + kg * 64 + 16 * t + 4 * lg);
                         const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
+                        uint4 av[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t w = wd[q];
+                            av[q] = uint4{w4_bf16x2(w, nib_mask, bf_magic), w4_bf16x2(w >> 4, nib_mask, bf_magic),
+                                          w4_bf16x2(w >> 8, nib_mask, bf_magic), w4_bf16x2(w >> 12, nib_mask, bf_magic)};
+                        }
 #pragma unroll
                         for (int c = 0; c < NT; ++c) {
                             if (c < ntiles) {
                                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                                for (int q = 0; q < 4; ++q) {
-                                    const uint32_t w = wd[q];
-                                    const uint4 av = {(w & 0x000F000Fu) | 0x43004300u,
-                                                      ((w >> 4) & 0x000F000Fu) | 0x43004300u,
-                                                      ((w >> 8) & 0x000F000Fu) | 0x43004300u,
-                                                      ((w >> 12) & 0x000F000Fu) | 0x43004300u};
-                                    a = Opnd<MOE_BF16>::mfma(av, tb[c][4 * kg + q], a);
-                                }
+                                for (int q = 0; q < 4; ++q) a = Opnd<MOE_BF16>::mfma(av[q], tb[c][4 * kg + q], a);
 #pragma unroll
                                 for (int v = 0; v < 4; ++v)
                                     acc[gg][t][c][v] = __builtin_fmaf(s4[v], a[v] - 136.0f * xs[c][v], acc[gg][t][c][v]);
@@ -1903,15 +1917,19 @@ template <int KIND, int NT>
 static hipError_t launch_decode_w4_nt(const GemmArgs& a, int nslots, hipStream_t s) {
     // an int4 row holds a quarter of a bf16 row's bytes: the gate/up GEMM takes
     // four row groups per workgroup with one token tile (as many copy steps
-    // per wavefront as bf16 with one group), two with two tiles (registers);
-    // the down GEMM two when that still leaves 256 workgroups
+    // per wavefront as bf16 with one group); the down GEMM two when that
+    // still leaves 256 workgroups
     const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
-    if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
-        if (a.ksplit == 1 && ncols % 128 == 0) return launch_decode_w4_g<KIND, NT, NT == 1 ? 4 : 2>(a, nslots, s);
-    } else {
-        if (a.ksplit == 1 && ncols % 128 == 0 && (long)(ncols / 128) * nslots >= 256)
-            return launch_decode_w4_g<KIND, NT, 2>(a, nslots, s);
+    if constexpr (NT == 1) {
+        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+            if (a.ksplit == 1 && ncols % 128 == 0) return launch_decode_w4_g<KIND, NT, 4>(a, nslots, s);
+        } else {
+            if (a.ksplit == 1 && ncols % 128 == 0 && (long)(ncols / 128) * nslots >= 256)
+                return launch_decode_w4_g<KIND, NT, 2>(a, nslots, s);
+        }
     }
+    // two token tiles: one row group, so the kernel fits two wavefronts per
+    // SIMD (the two token-value buffers take 128 registers per lane)
     return launch_decode_w4_g<KIND, NT, 1>(a, nslots, s);
 }
 
