@@ -1650,7 +1650,8 @@ hipError_t launch_down_combine(const GemmCall& c, const float* topk_weights, voi
 //   sum_k W[n][k] x[k] = s[g][n] * (sum_k (128 + u_k) x_k - 136 * sum_k x_k),
 // the token sums coming from an MFMA with an all-ones operand.  Each MFMA
 // covers 32 k of one group (lane group lg: k = 128 g + 32 lg + 8 q + j), so
-// every group's products are accumulated apart and scaled per row.
+// every group's products are accumulated apart (starting from -136 * sum x)
+// and scaled per row.
 
 // Two codes of a word (bits 0-3 and 16-19 of w) as two bf16 words 128 + u:
 // (w & 0x000F000F) | 0x43004300 in one v_and_or_b32.
@@ -1800,6 +1801,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
                         if (c < ntiles)
 #pragma unroll
                             for (int q = 0; q < 4; ++q) xs[c] = Opnd<MOE_BF16>::mfma(ones, tb[c][4 * kg + q], xs[c]);
+                        xs[c] *= -136.0f;  // the row products start from -136 * sum x
                     }
 #pragma unroll
                     for (int t = 0; t < T; ++t) {
@@ -1817,12 +1819,12 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
 #pragma unroll
                         for (int c = 0; c < NT; ++c) {
                             if (c < ntiles) {
-                                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                                f32x4 a = xs[c];
 #pragma unroll
                                 for (int q = 0; q < 4; ++q) a = Opnd<MOE_BF16>::mfma(av[q], tb[c][4 * kg + q], a);
 #pragma unroll
                                 for (int v = 0; v < 4; ++v)
-                                    acc[gg][t][c][v] = __builtin_fmaf(s4[v], a[v] - 136.0f * xs[c][v], acc[gg][t][c][v]);
+                                    acc[gg][t][c][v] = __builtin_fmaf(s4[v], a[v], acc[gg][t][c][v]);
                             }
                         }
                     }
