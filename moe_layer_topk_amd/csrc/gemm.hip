@@ -835,6 +835,13 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
             brow[j] = wn * C::WTN + 32 * j + (lane & 31);
     }
     const int khalf = lane >> 5;  // which half of a K substep this lane holds
+    // the tile's real rows are a prefix (an expert's last tile is padded):
+    // 32-row MFMA tiles past them are skipped, fragment reads included.  The
+    // copies still stream the whole weight tile, which is what a mostly empty
+    // tile waits on: measured 1.4% on the e4m3 layer at 512 tokens (half of
+    // each tile padding), neutral on the 128-expert layer at 2048 tokens
+    const int nreal = min(C::BM, g.offsets[e] + g.counts[e] - mtile * C::BM);
+    const int live_tm = __builtin_amdgcn_readfirstlane(min(C::TM, max(0, (nreal - wm * C::WTM + 31) / 32)));
 
     float scale = 1.0f;
     if constexpr (DT == MOE_FP8_E4M3) {
@@ -849,8 +856,9 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
     // one stage; PF: the copies of stage kt + ST - 1 are issued during it (every
     // stage but the last ST - 1, which run as a separate tail so that the main
     // loop carries no per-copy condition)
-    auto stage = [&](int kt, auto pf_tag) {
+    auto stage = [&](int kt, auto pf_tag, auto lt_tag) {
         constexpr bool pf = decltype(pf_tag)::value;
+        constexpr int LT = decltype(lt_tag)::value;  // live 32-row MFMA tiles of this wave
         if constexpr (pf) {
             wait_vm<(C::ST - 2) * C::L < 64 ? (C::ST - 2) * C::L : 63>();  // stage kt landed; ST - 2 later ones in flight
         } else {
@@ -874,7 +882,7 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
             for (int h = 0; h < Mf::kChunks; ++h) {
                 const int c = (ks * 2 + khalf) * Mf::kChunks + h;  // logical 16-byte chunk
 #pragma unroll
-                for (int i = 0; i < C::TM; ++i)
+                for (int i = 0; i < LT; ++i)
                     af[buf][i][h] = *reinterpret_cast<const uint4*>(sa + arow[i] * C::RowBytes + (C::swz(c, arow[i]) << 4));
 #pragma unroll
                 for (int j = 0; j < C::TN; ++j)
@@ -894,7 +902,7 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
 #pragma unroll
             for (int q = 0; q < C::TM * C::TN; ++q) {
                 const int i = q / C::TN, j = q % C::TN;
-                acc[i][j] = Mf::run(af[cur][i], bfr[cur][j], acc[i][j]);
+                if (i < LT) acc[i][j] = Mf::run(af[cur][i], bfr[cur][j], acc[i][j]);
                 if ((q + 1) % kGap == 0) {
                     const int jj = ks * kPer + (q + 1) / kGap - 1;
                     if (pf && (q + 1) / kGap <= kPer && jj < C::L) {
@@ -914,8 +922,21 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
         }
     };
     const int nmain = nk - (C::ST - 1) > 0 ? nk - (C::ST - 1) : 0;
-    for (int kt = 0; kt < nmain; ++kt) stage(kt, std::true_type{});
-    for (int kt = nmain; kt < nk; ++kt) stage(kt, std::false_type{});
+    auto kloop = [&](auto lt_tag) {
+        for (int kt = 0; kt < nmain; ++kt) stage(kt, std::true_type{}, lt_tag);
+        for (int kt = nmain; kt < nk; ++kt) stage(kt, std::false_type{}, lt_tag);
+    };
+    // one branch per tile: the loop of a wave with all its rows real has no
+    // per-MFMA condition
+    static_assert(C::TM <= 2, "live tile counts 0, 1 and TM only");
+    if (live_tm == C::TM) {
+        kloop(std::integral_constant<int, C::TM>{});
+    } else if constexpr (C::TM > 1) {
+        if (live_tm == 1) kloop(std::integral_constant<int, 1>{});
+        else kloop(std::integral_constant<int, 0>{});
+    } else {
+        kloop(std::integral_constant<int, 0>{});
+    }
 
     // ---- epilogue: lane holds C[8*(v/4) + 4*(lane/32) + v%4][lane%32] of each 32x32 tile
     float amax = 0.0f;
