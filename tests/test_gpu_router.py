@@ -37,7 +37,9 @@ def rel_err(gpu, ref):
 
 
 ROUTER_SHAPES = [("bf16", 1, 8, 4096), ("bf16", 300, 8, 4096), ("bf16", 33, 128, 2048), ("f32", 16, 8, 256),
-                 ("fp8", 70, 64, 4096), ("bf16", 5, 256, 128)]
+                 ("fp8", 70, 64, 4096), ("bf16", 5, 256, 128),
+                 # 8 tokens x 4 experts per wavefront, E not a multiple of 4, H an odd multiple of 128
+                 ("bf16", 2048, 130, 384), ("f32", 9, 3, 384)]
 
 
 @pytest.mark.parametrize("dtype,M,E,H", ROUTER_SHAPES)
