@@ -244,3 +244,34 @@ def test_cache_mixtral_decode_steps(dev, dtype):
     cache.close()
     del w
     torch.cuda.empty_cache()
+
+
+def test_cache_prefill_batch(dev):
+    """A 1024-token batch (128 pairs per expert: the tile kernels) through a
+    cache that holds every expert: the same bits as the resident layer; and a
+    batch routed to 8 of 16 experts through an 8-slot cache, against the
+    oracle (the slot count changes the tile-height choice, so bits may
+    differ from the resident layer's)."""
+    import moe_layer_topk_amd as moe
+    cfg = small("bf16", E=16, topk=2, H=512, I=512)
+    w = layer_weights(cfg, dev)
+    wh = host_parts(w)
+    cache = make_cache(moe, wh, 16, dev)
+    b = layer_batch(cfg, 1024, dev, seed=600)
+    out = cache(b["x"], b["logits"], cfg.topk)
+    assert torch.equal(out, fused(moe, cfg, w, b))
+    cache.close()
+    cache = make_cache(moe, wh, 8, dev)
+    b = layer_batch(cfg, 512, dev, seed=601)
+    b["logits"][:, 8:] -= 100.0  # route among experts 0..7 only
+    ids = torch.empty((512, 2), dtype=torch.int32, device=dev)
+    out = cache(b["x"], b["logits"], cfg.topk, topk_ids=ids)
+    torch.cuda.synchronize()
+    assert int(ids.max()) < 8
+    bh = {k: (v.cpu() if v is not None else None) for k, v in b.items()}
+    tok = np.arange(0, 512, 17)
+    ref = oracle.moe_layer("bf16", bh["x"], None, bh["logits"], wh["w1"], None, wh["w2"], None, cfg.topk, tokens=tok)
+    g = out.float().cpu().numpy().astype(np.float64)[tok]
+    assert np.abs(g - ref).max() <= TOL["bf16"] * np.abs(ref).max()
+    assert cache.stats()["misses"] == 8
+    cache.close()
