@@ -1938,21 +1938,27 @@ static hipError_t launch_decode_w4_g(const GemmArgs& a, int nslots, hipStream_t 
 
 template <int KIND, int NT>
 static hipError_t launch_decode_w4_nt(const GemmArgs& a, int nslots, hipStream_t s) {
-    // an int4 row holds a quarter of a bf16 row's bytes: the gate/up GEMM takes
-    // four row groups per workgroup with one token tile (as many copy steps
-    // per wavefront as bf16 with one group); the down GEMM two when that
-    // still leaves 256 workgroups
+    // The int4 kernel is bound by its ALU work and one workgroup per CU leaves
+    // one wavefront per SIMD: with one token tile the gate/up GEMM takes the
+    // most row groups (4, 2, 1) that still give about 400 workgroups, the
+    // down GEMM two groups from 512 workgroups (measured on the Mixtral and
+    // 128-expert int4 layers against four and two fixed groups: 128 experts
+    // at one token 32.1 -> 25.0 us, Mixtral at one token 56.3 -> 50.7, at 8
+    // tokens 156.9 -> 147.2).  With two token tiles, one group (registers).
     const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
     if constexpr (NT == 1) {
-        if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
-            if (a.ksplit == 1 && ncols % 128 == 0) return launch_decode_w4_g<KIND, NT, 4>(a, nslots, s);
-        } else {
-            if (a.ksplit == 1 && ncols % 128 == 0 && (long)(ncols / 128) * nslots >= 256)
-                return launch_decode_w4_g<KIND, NT, 2>(a, nslots, s);
+        if (a.ksplit == 1) {
+            if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
+                if (ncols % 128 == 0 && (long)(ncols / 128) * nslots >= 400)
+                    return launch_decode_w4_g<KIND, NT, 4>(a, nslots, s);
+                if (ncols % 64 == 0 && (long)(ncols / 64) * nslots >= 400)
+                    return launch_decode_w4_g<KIND, NT, 2>(a, nslots, s);
+            } else {
+                if (ncols % 128 == 0 && (long)(ncols / 128) * nslots >= 512)
+                    return launch_decode_w4_g<KIND, NT, 2>(a, nslots, s);
+            }
         }
     }
-    // two token tiles: one row group, so the kernel fits two wavefronts per
-    // SIMD (the two token-value buffers take 128 registers per lane)
     return launch_decode_w4_g<KIND, NT, 1>(a, nslots, s);
 }
 
