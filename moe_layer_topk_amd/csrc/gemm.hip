@@ -2078,13 +2078,17 @@ static hipError_t launch_decode_ntg(const GemmArgs& a, int nslots, hipStream_t s
 template <int KIND, int DT, int NT>
 static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_est, hipStream_t s) {
     // Two row groups per workgroup (twice the weight rows per token load):
-    // measured on the Mixtral, 128-expert and e4m3 decode layers, the down
-    // GEMM gains from 256 workgroups up, the gate/up GEMM only for bf16 with
-    // two token tiles and at least 512 workgroups.
+    // measured on the Mixtral, 128-expert and e4m3 decode layers, the bf16
+    // down GEMM gains from 256 workgroups up (Mixtral shape at 8 to 64 tokens:
+    // 3-4% over one group), the gate/up GEMM only for bf16 with two token
+    // tiles and at least 512 workgroups; the e4m3 down GEMM with one token
+    // tile (token values quantised in registers) is as fast or faster with
+    // one (64-expert layer at 8 tokens: 246 -> 233 us)
     const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
     const int rows2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? 64 : 128;
-    const bool two = (KIND == MOE_GEMM_DOWN) ? (NT < 4 && (long)(ncols / rows2) * active_est >= 256)
-                                             : (DT == MOE_BF16 && NT == 2 && (long)(ncols / rows2) * active_est >= 512);
+    const bool two = (KIND == MOE_GEMM_DOWN)
+                         ? (NT < 4 && !(DT == MOE_FP8_E4M3 && NT == 1) && (long)(ncols / rows2) * active_est >= 256)
+                         : (DT == MOE_BF16 && NT == 2 && (long)(ncols / rows2) * active_est >= 512);
     if constexpr (KIND == MOE_GEMM_GATE_UP_SILU && NT < 4) {
         // four row groups per workgroup for the gate/up GEMM: always for
         // e4m3 (a row holds half the bytes of a bf16 one, so one group is few
