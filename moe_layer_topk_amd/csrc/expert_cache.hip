@@ -261,6 +261,8 @@ moe_status fused_moe_cached(moe_expert_cache* c, const void* x, const float* x_s
         hipStreamSynchronize(s) != hipSuccess)
         return MOE_ERR_HIP;
     std::vector<int32_t> need(host_ids, host_ids + P);
+    for (int32_t e : need)
+        if (e < 0 || e >= E) return MOE_ERR_HIP;  // not a routing result (the route kernel writes [0, E))
     std::sort(need.begin(), need.end());
     need.erase(std::unique(need.begin(), need.end()), need.end());
     if ((int32_t)need.size() > C) return MOE_ERR_UNSUPPORTED;  // more experts than slots in one batch
