@@ -202,7 +202,12 @@ size_t fused_moe_workspace_size(moe_dtype dtype, int32_t M, int32_t E, int32_t t
  *                 routing result (NULL to skip)
  *  H and I must be multiples of 128 (of 256 for MOE_FP8_E4M3 and MOE_W4A16).
  *  workspace      device, >= fused_moe_workspace_size(...) bytes, 256-byte
- *                 aligned; its contents on entry do not matter. */
+ *                 aligned; its contents on entry do not matter.
+ * Kernel choice (not results beyond rounding order; read at each call):
+ *  MOE_GEMM_PATH=decode|prefill forces the decode kernels or the tile
+ *  kernels (64-row tiles); MOE_DOWN_COMBINE=1 lets a bf16 decode batch of
+ *  about one token tile per expert run the down GEMM with the combine inside
+ *  (the same bits as the separate combine, not faster on MI355X). */
 moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const float* router_logits,
                      const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
                      int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I, int32_t renormalize,
