@@ -15,10 +15,14 @@
  * Conventions for every call:
  *  - Pointers named as device pointers must point to device memory of the
  *    current HIP device and be 16-byte aligned.  The library never
- *    allocates, frees or keeps a pointer after a call returns.
+ *    allocates, frees or keeps a pointer after a call returns, except the
+ *    expert cache (moe_cache_*), which keeps the host and slot pointers it is
+ *    created with and allocates host bookkeeping and HIP events.
+ *  - Calls return without waiting for the device, except fused_moe_cached,
+ *    which waits for its own routing (the miss path needs the ids).
  *  - Every call enqueues work on `stream` (a hipStream_t passed as void*;
- *    NULL is the null stream) and returns without synchronising.  Device
- *    faults surface at the caller's next synchronisation.
+ *    NULL is the null stream).  Device faults surface at the caller's next
+ *    synchronisation.
  *  - Arguments are validated on the host before any HIP call; a rejected
  *    call enqueues nothing.  M = 0 is a valid no-op.
  *  - Matrices are row-major.  Outputs are overwritten, never accumulated.
