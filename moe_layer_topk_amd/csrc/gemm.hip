@@ -1675,11 +1675,20 @@ hipError_t launch_down_combine(const GemmCall& c, const float* topk_weights, voi
 // and scaled per row.
 
 // Two codes of a word (bits 0-3 and 16-19 of w) as two bf16 words 128 + u:
-// (w & 0x000F000F) | 0x43004300 in one v_and_or_b32.
+// (w & 0x000F000F) | 0x43004300, one v_and_or_b32 when both constants sit in
+// registers the compiler cannot see through (w4_opaque).  Written in C, not
+// asm, so that the compiler knows the result is a vector ALU write and keeps
+// the wait states an MFMA reading it needs.
 __device__ __forceinline__ uint32_t w4_bf16x2(uint32_t w, uint32_t mask, uint32_t magic) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "v"(mask), "v"(magic));
-    return r;
+    return (w & mask) | magic;
+}
+
+// a constant held in a vector register and hidden from constant folding: a
+// folded mask and magic become two literal-operand instructions, since the
+// fused AND-OR (VOP3) takes no literal on this target
+__device__ __forceinline__ uint32_t w4_opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 template <int KIND, int NT, int G, int KD>
@@ -1689,6 +1698,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
     constexpr int kScaleOff = 64 * kRingSB;   // [2 groups][64 rows] float32 after the codes
     constexpr int kStage = 64 * kRingSB + 1024;
     static_assert(KD == 2, "the scale copy of step j+2 goes to step j's slot");
+    static_assert(NT == 1 || NT == 2, "live token tiles are NT or 1");
     extern __shared__ __attribute__((aligned(1024))) char w4_lds[];
 
     const int slot = blockIdx.y;
@@ -1732,10 +1742,9 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
     const unsigned ring_lds0 = lds_addr_of(ring);
     f32x4* red = reinterpret_cast<f32x4*>(w4_lds);  // after the main loop only
     const uint4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
-    // the AND-OR constants in registers: the fused v_and_or_b32 (VOP3) takes
-    // no literal on this target
-    const uint32_t nib_mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
-    const uint32_t bf_magic = __builtin_amdgcn_readfirstlane(0x43004300u);
+    // the AND-OR constants in registers
+    const uint32_t nib_mask = w4_opaque(0x000F000Fu);
+    const uint32_t bf_magic = w4_opaque(0x43004300u);
 
     for (int pass = 0; pass < cnt; pass += NT * 16) {
         const int ntiles = min(NT, (cnt - pass + 15) / 16);
@@ -1810,46 +1819,62 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
             const float* sc = reinterpret_cast<const float*>(st + kScaleOff);
             const int gi = (wave + 4 * j) / nks;
             const int sw = (lr >> 1) & 7;
+            // LT live token tiles, fixed per pass: the loops below carry no
+            // per-tile branch, so the compiler can overlap one tile's AND-ORs
+            // with the MFMAs of another and the chains of the LT tiles
+            // interleave (each MFMA's accumulator comes from the one before)
+            auto body = [&](auto lt_tag) {
+                constexpr int LT = decltype(lt_tag)::value;
 #pragma unroll
-            for (int gg = 0; gg < G; ++gg) {
-                if (gg != gi) continue;
+                for (int gg = 0; gg < G; ++gg) {
+                    if (gg != gi) continue;
 #pragma unroll
-                for (int kg = 0; kg < 2; ++kg) {
-                    f32x4 xs[NT];
+                    for (int kg = 0; kg < 2; ++kg) {
+                        f32x4 xs[LT];
 #pragma unroll
-                    for (int c = 0; c < NT; ++c) {
-                        xs[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        if (c < ntiles)
+                        for (int c = 0; c < LT; ++c) xs[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) xs[c] = Opnd<MOE_BF16>::mfma(ones, tb[c][4 * kg + q], xs[c]);
-                        xs[c] *= -136.0f;  // the row products start from -136 * sum x
-                    }
+                        for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int t = 0; t < T; ++t) {
-                        const uint4 wq =
-                            *reinterpret_cast<const uint4*>(st + (16 * t + lr) * kRingSB + (((4 * kg + lg) ^ sw) << 4));
-                        const f32x4 s4 = *reinterpret_cast<const f32x4*>(sc + kg * 64 + 16 * t + 4 * lg);
-                        const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
-                        uint4 av[4];
+                            for (int c = 0; c < LT; ++c) xs[c] = Opnd<MOE_BF16>::mfma(ones, tb[c][4 * kg + q], xs[c]);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const uint32_t w = wd[q];
-                            av[q] = uint4{w4_bf16x2(w, nib_mask, bf_magic), w4_bf16x2(w >> 4, nib_mask, bf_magic),
-                                          w4_bf16x2(w >> 8, nib_mask, bf_magic), w4_bf16x2(w >> 12, nib_mask, bf_magic)};
-                        }
+                        for (int c = 0; c < LT; ++c) xs[c] *= -136.0f;  // the row products start from -136 * sum x
 #pragma unroll
-                        for (int c = 0; c < NT; ++c) {
-                            if (c < ntiles) {
-                                f32x4 a = xs[c];
+                        for (int t = 0; t < T; ++t) {
+                            const uint4 wq =
+                                *reinterpret_cast<const uint4*>(st + (16 * t + lr) * kRingSB + (((4 * kg + lg) ^ sw) << 4));
+                            const f32x4 s4 = *reinterpret_cast<const f32x4*>(sc + kg * 64 + 16 * t + 4 * lg);
+                            const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
+                            uint4 av[4];
 #pragma unroll
-                                for (int q = 0; q < 4; ++q) a = Opnd<MOE_BF16>::mfma(av[q], tb[c][4 * kg + q], a);
+                            for (int q = 0; q < 4; ++q) {
+                                const uint32_t w = wd[q];
+                                av[q] = uint4{w4_bf16x2(w, nib_mask, bf_magic), w4_bf16x2(w >> 4, nib_mask, bf_magic),
+                                              w4_bf16x2(w >> 8, nib_mask, bf_magic), w4_bf16x2(w >> 12, nib_mask, bf_magic)};
+                            }
+                            f32x4 a[LT];
+#pragma unroll
+                            for (int c = 0; c < LT; ++c) a[c] = xs[c];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                                for (int c = 0; c < LT; ++c) a[c] = Opnd<MOE_BF16>::mfma(av[q], tb[c][4 * kg + q], a[c]);
+#pragma unroll
+                            for (int c = 0; c < LT; ++c)
 #pragma unroll
                                 for (int v = 0; v < 4; ++v)
-                                    acc[gg][t][c][v] = __builtin_fmaf(s4[v], a[v], acc[gg][t][c][v]);
-                            }
+                                    acc[gg][t][c][v] = __builtin_fmaf(s4[v], a[c][v], acc[gg][t][c][v]);
                         }
                     }
                 }
+            };
+            if constexpr (NT > 1) {
+                if (ntiles == NT)
+                    body(std::integral_constant<int, NT>{});
+                else
+                    body(std::integral_constant<int, 1>{});
+            } else {
+                body(std::integral_constant<int, 1>{});
             }
             // refill this buffer with step j + 2's values (the last steps reload
             // step nw-1, unused: a conditional refill would merge register
