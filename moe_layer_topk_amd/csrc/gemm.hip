@@ -1657,13 +1657,15 @@ hipError_t launch_down_combine(const GemmCall& c, const float* topk_weights, voi
 // stream through a wavefront-private LDS ring of direct-to-LDS copies (as
 // in the ring kernel, non-temporal), one more copy per stage brings the
 // step's group scales of the 64 rows.  The token values of a step (bf16)
-// come through registers two steps ahead, as in the ring kernel's e4m3
-// down projection: the loads of step j+2 follow the wait that retires step
-// j's copies, and the scale copy of step j+2 follows them (into step j's
-// slot, whose reads are done), so the only copies younger than a step's
-// token loads when they are consumed are the next stage's 8 weight copies,
-// which the compiler's own wait (it counts the 8 younger token loads) leaves
-// in flight.
+// come through registers, two buffers in fixed roles.  Step j begins with
+// a wait for every vector-memory operation of the wave (a wait the compiler
+// sees, so it adds none of its own before the token values are used: it
+// cannot count the copies, which are asm, and any wait it placed later
+// would also retire the next step's loads); what is in flight then is
+// exactly step j's scales, codes and token values, issued at the start of
+// step j - 1.  It then issues step j + 1's (the scales and codes into step
+// j - 1's slot, whose reads are done, the token values into step j - 1's
+// buffer), which load during step j's products.
 //
 // Products on the bf16 MFMA without converting codes to values: OR-ing a
 // code into 0x4300 gives the bf16 128 + u exactly, so one AND-OR turns a
@@ -1797,24 +1799,26 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
 #pragma unroll
                 for (int c = 0; c < NT; ++c) acc[gi][t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+        // step 0's token values first: their addresses wait on the row-id
+        // loads, and a wait placed after the copies would retire those too
         uint4 tb0[NT][8], tb1[NT][8];
         tload(tb0, 0);
-        tload(tb1, nw > 1 ? 1 : 0);
         if (0 < nw) {
-            issue(0);
             issue_scales(0);
+            issue(0);
         }
-        if (1 < nw) issue_scales(1);
 
-        auto step = [&](int j, uint4 (&tb)[NT][8]) {
+        // tb holds step j's token values, tn is refilled with step j + 1's
+        // (unconditionally: the last step reloads step nw-1, unused, since a
+        // conditional refill would merge two register states and the copies
+        // that merge needs would wait on these very loads)
+        auto step = [&](int j, uint4 (&tb)[NT][8], uint4 (&tn)[NT][8]) {
+            wait_vm<0>();
             if (j + 1 < nw) {
+                issue_scales(j + 1);
                 issue(j + 1);
-                ring_wait_vm<kWInstr>();
-            } else {
-                ring_wait_vm<0>();
             }
-            // every vector-memory operation older than the copies just issued
-            // has completed: this step's codes, scales and token values
+            tload(tn, min(j + 1, nw - 1));
             const char* st = ring + (j % KD) * kStage;
             const float* sc = reinterpret_cast<const float*>(st + kScaleOff);
             const int gi = (wave + 4 * j) / nks;
@@ -1876,18 +1880,13 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
             } else {
                 body(std::integral_constant<int, 1>{});
             }
-            // refill this buffer with step j + 2's values (the last steps reload
-            // step nw-1, unused: a conditional refill would merge register
-            // states), then step j + 2's scales into this step's slot
-            tload(tb, min(j + 2, nw - 1));
-            if (j + 2 < nw) issue_scales(j + 2);
         };
         int j = 0;
         for (; j + 1 < nw; j += 2) {
-            step(j, tb0);
-            step(j + 1, tb1);
+            step(j, tb0, tb1);
+            step(j + 1, tb1, tb0);
         }
-        if (j < nw) step(j, tb0);
+        if (j < nw) step(j, tb0, tb1);
 
         // every wave is done with its ring: the reduction area aliases it
         __syncthreads();
