@@ -1760,7 +1760,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
             trow[c] = reinterpret_cast<const char*>(g.a) + (size_t)src * K * 2 + 64 * lg;
         }
         // the codes of step j (8 copies)
-        auto issue = [&](int j) {
+        auto issue = [&](int j) __attribute__((always_inline)) {
             const int s = wave + 4 * j;
             const int gi = s / nks, ks = ks0 + s % nks;
             const unsigned st = ring_lds0 + (unsigned)((j % KD) * kStage);
@@ -1770,19 +1770,20 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
             for (int i = 0; i < kWInstr; ++i) lds_dma16_nt_at(wsrc + woff[i], st + i * 1024);
         };
         // the group scales of step j (one copy)
-        auto issue_scales = [&](int j) {
+        auto issue_scales = [&](int j) __attribute__((always_inline)) {
             const int s = wave + 4 * j;
             const int gi = s / nks, ks = ks0 + s % nks;
             const unsigned st = ring_lds0 + (unsigned)((j % KD) * kStage);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             lds_dma16_at(sexp + (size_t)(2 * ks + skg) * N + srow + gi * grows, st + kScaleOff);
         };
-        // the bf16 token values of step j: 8 x 16 bytes per tile (values
-        // 128 kg + 32 lg + 8 q .. + 7 of the step, kg = 0..1, q = 0..3)
-        auto tload = [&](uint4 (&b)[NT][8], int j) {
+        // the bf16 token values of step j for LT live tiles: 8 x 16 bytes per
+        // tile (values 128 kg + 32 lg + 8 q .. + 7 of the step, kg = 0..1,
+        // q = 0..3)
+        auto tload = [&](uint4 (&b)[NT][8], int j, auto lt_tag) __attribute__((always_inline)) {
             const int ks = ks0 + (wave + 4 * j) % nks;
 #pragma unroll
-            for (int c = 0; c < NT; ++c) {
+            for (int c = 0; c < decltype(lt_tag)::value; ++c) {
                 const char* src = trow[c] + (size_t)ks * (2 * 2 * kRingSB);
 #pragma unroll
                 for (int kg = 0; kg < 2; ++kg)
@@ -1799,35 +1800,26 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
 #pragma unroll
                 for (int c = 0; c < NT; ++c) acc[gi][t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // step 0's token values first: their addresses wait on the row-id
-        // loads, and a wait placed after the copies would retire those too
         uint4 tb0[NT][8], tb1[NT][8];
-        tload(tb0, 0);
-        if (0 < nw) {
-            issue_scales(0);
-            issue(0);
-        }
-
         // tb holds step j's token values, tn is refilled with step j + 1's
         // (unconditionally: the last step reloads step nw-1, unused, since a
         // conditional refill would merge two register states and the copies
         // that merge needs would wait on these very loads)
-        auto step = [&](int j, uint4 (&tb)[NT][8], uint4 (&tn)[NT][8]) {
+        auto step = [&](int j, uint4 (&tb)[NT][8], uint4 (&tn)[NT][8], auto lt_tag) __attribute__((always_inline)) {
             wait_vm<0>();
             if (j + 1 < nw) {
                 issue_scales(j + 1);
                 issue(j + 1);
             }
-            tload(tn, min(j + 1, nw - 1));
+            tload(tn, min(j + 1, nw - 1), lt_tag);
             const char* st = ring + (j % KD) * kStage;
             const float* sc = reinterpret_cast<const float*>(st + kScaleOff);
             const int gi = (wave + 4 * j) / nks;
             const int sw = (lr >> 1) & 7;
-            // LT live token tiles, fixed per pass: the loops below carry no
-            // per-tile branch, so the compiler can overlap one tile's AND-ORs
-            // with the MFMAs of another and the chains of the LT tiles
-            // interleave (each MFMA's accumulator comes from the one before)
-            auto body = [&](auto lt_tag) {
+            // the compiler can overlap one tile's AND-ORs with the MFMAs of
+            // another and interleave the LT tiles' MFMA chains (each MFMA's
+            // accumulator comes from the one before)
+            auto body = [&](auto lt_tag) __attribute__((always_inline)) {
                 constexpr int LT = decltype(lt_tag)::value;
 #pragma unroll
                 for (int gg = 0; gg < G; ++gg) {
@@ -1872,21 +1864,34 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
                     }
                 }
             };
-            if constexpr (NT > 1) {
-                if (ntiles == NT)
-                    body(std::integral_constant<int, NT>{});
-                else
-                    body(std::integral_constant<int, 1>{});
-            } else {
-                body(std::integral_constant<int, 1>{});
-            }
+            body(lt_tag);
         };
-        int j = 0;
-        for (; j + 1 < nw; j += 2) {
-            step(j, tb0, tb1);
-            step(j + 1, tb1, tb0);
+        // LT live token tiles, fixed per pass: a pass whose rows fit in fewer
+        // tiles than NT loads and multiplies only those, and its loop carries
+        // no per-tile branch
+        auto steps = [&](auto lt_tag) __attribute__((always_inline)) {
+            // step 0's token values first: their addresses wait on the row-id
+            // loads, and a wait placed after the copies would retire those too
+            tload(tb0, 0, lt_tag);
+            if (0 < nw) {
+                issue_scales(0);
+                issue(0);
+            }
+            int j = 0;
+            for (; j + 1 < nw; j += 2) {
+                step(j, tb0, tb1, lt_tag);
+                step(j + 1, tb1, tb0, lt_tag);
+            }
+            if (j < nw) step(j, tb0, tb1, lt_tag);
+        };
+        if constexpr (NT > 1) {
+            if (ntiles == NT)
+                steps(std::integral_constant<int, NT>{});
+            else
+                steps(std::integral_constant<int, 1>{});
+        } else {
+            steps(std::integral_constant<int, 1>{});
         }
-        if (j < nw) step(j, tb0, tb1);
 
         // every wave is done with its ring: the reduction area aliases it
         __syncthreads();
