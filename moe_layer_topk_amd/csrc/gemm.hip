@@ -1150,7 +1150,9 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
                 }
         }
 
-        auto issue = [&](int j) {
+        // the copies of step j: the weight rows, then the token rows of the
+        // pass's LT live tiles
+        auto issue = [&](int j, auto lt_tag) __attribute__((always_inline)) {
             const int s = wave + 4 * j;
             const int gi = s / nks, ks = ks0 + s % nks;
             const unsigned st = ring_lds0 + (unsigned)((j % KD) * R::Stage);
@@ -1162,7 +1164,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
             if constexpr (!TQ) {
                 const char* tsrc = reinterpret_cast<const char*>(g.a) + (size_t)ks * kRingSB;
 #pragma unroll
-                for (int c = 0; c < NT; ++c)
+                for (int c = 0; c < decltype(lt_tag)::value; ++c)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
                         lds_dma16_at(tsrc + toff[c][h], st + R::TokOff + (2 * c + h) * 1024);
@@ -1196,16 +1198,15 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
             tload(tb[0], 0);
             tload(tb[1], nw > 1 ? 1 : 0);
         }
-#pragma unroll
-        for (int j = 0; j < KD - 1; ++j)
-            if (j < nw) issue(j);
         // one step of the ring; TQ: tbuf holds step j's token values and is
         // refilled with step j + 2's (two buffers in fixed roles, so no
         // register copy makes the compiler wait on the loads just issued)
-        auto step = [&](int j, uint4 (&tbuf)[TQ ? 8 : 1]) {
+        auto step = [&](int j, uint4 (&tbuf)[TQ ? 8 : 1], auto lt_tag) __attribute__((always_inline)) {
+            constexpr int LT = decltype(lt_tag)::value;
+            constexpr int kInstr = R::WInstr + (TQ ? 0 : LT * 16 * kRingSB / 1024);  // copies per step
             if (j + KD - 1 < nw) {
-                issue(j + KD - 1);
-                ring_wait_vm<(KD - 1) * R::Instr>();
+                issue(j + KD - 1, lt_tag);
+                ring_wait_vm<(KD - 1) * kInstr>();
             } else {
                 ring_wait_vm<0>();
             }
@@ -1241,15 +1242,13 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
                         for (int t = 0; t < T; ++t) acc[gg][t][0] = mfma_f8_16x16x128(a0[t], a1[t], tq0, tq1, acc[gg][t][0]);
                     } else {
 #pragma unroll
-                        for (int c = 0; c < NT; ++c) {
-                            if (c < ntiles) {
-                                const char* bp = st + R::TokOff + (16 * c + lr) * kRingSB;
-                                const uint4 b0 = *reinterpret_cast<const uint4*>(bp + ((lg ^ sw) << 4));
-                                const uint4 b1 = *reinterpret_cast<const uint4*>(bp + (((lg + 4) ^ sw) << 4));
+                        for (int c = 0; c < LT; ++c) {
+                            const char* bp = st + R::TokOff + (16 * c + lr) * kRingSB;
+                            const uint4 b0 = *reinterpret_cast<const uint4*>(bp + ((lg ^ sw) << 4));
+                            const uint4 b1 = *reinterpret_cast<const uint4*>(bp + (((lg + 4) ^ sw) << 4));
 #pragma unroll
-                                for (int t = 0; t < T; ++t)
-                                    acc[gg][t][c] = mfma_f8_16x16x128(a0[t], a1[t], b0, b1, acc[gg][t][c]);
-                            }
+                            for (int t = 0; t < T; ++t)
+                                acc[gg][t][c] = mfma_f8_16x16x128(a0[t], a1[t], b0, b1, acc[gg][t][c]);
                         }
                     }
                 } else {
@@ -1262,26 +1261,44 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
                         for (int t = 0; t < T; ++t)
                             a[t] = *reinterpret_cast<const uint4*>(st + (16 * t + lr) * kRingSB + pc);
 #pragma unroll
-                        for (int c = 0; c < NT; ++c) {
-                            if (c < ntiles) {
-                                const uint4 b = *reinterpret_cast<const uint4*>(st + R::TokOff + (16 * c + lr) * kRingSB + pc);
+                        for (int c = 0; c < LT; ++c) {
+                            const uint4 b = *reinterpret_cast<const uint4*>(st + R::TokOff + (16 * c + lr) * kRingSB + pc);
 #pragma unroll
-                                for (int t = 0; t < T; ++t) acc[gg][t][c] = Opnd<MOE_BF16>::mfma(a[t], b, acc[gg][t][c]);
-                            }
+                            for (int t = 0; t < T; ++t) acc[gg][t][c] = Opnd<MOE_BF16>::mfma(a[t], b, acc[gg][t][c]);
                         }
                     }
                 }
             }
         };
-        if constexpr (TQ) {
-            int j = 0;
-            for (; j + 1 < nw; j += 2) {
-                step(j, tb[0]);
-                step(j + 1, tb[1]);
+        // LT token tiles copied and multiplied, fixed per pass: ntiles rounded
+        // up to 1, 2 or NT (the rows of a tile past the count repeat the
+        // last row; their products are not used), so a pass whose rows fit
+        // fewer tiles than NT copies fewer token rows, and the loop carries
+        // no per-tile branch
+        auto steps = [&](auto lt_tag) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < KD - 1; ++j)
+                if (j < nw) issue(j, lt_tag);
+            if constexpr (TQ) {
+                int j = 0;
+                for (; j + 1 < nw; j += 2) {
+                    step(j, tb[0], lt_tag);
+                    step(j + 1, tb[1], lt_tag);
+                }
+                if (j < nw) step(j, tb[0], lt_tag);
+            } else {
+                for (int j = 0; j < nw; ++j) step(j, tb[0], lt_tag);
             }
-            if (j < nw) step(j, tb[0]);
+        };
+        if constexpr (NT == 1) {
+            steps(std::integral_constant<int, 1>{});
         } else {
-            for (int j = 0; j < nw; ++j) step(j, tb[0]);
+            if (ntiles == 1)
+                steps(std::integral_constant<int, 1>{});
+            else if (NT > 2 && ntiles == 2)
+                steps(std::integral_constant<int, (NT > 2 ? 2 : NT)>{});
+            else
+                steps(std::integral_constant<int, NT>{});
         }
 
         // every wave is done with its ring: the reduction area aliases it
