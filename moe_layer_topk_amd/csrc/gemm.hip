@@ -1737,6 +1737,10 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
     const int nks = (int)((long)(blockIdx.z + 1) * nks_all / g.ksplit) - ks0;
     const int total = G * nks;
     const int nw = total > wave ? (total - wave + 3) / 4 : 0;
+    // step s of the workgroup: row group s / nks, K step s % nks (with one
+    // group, s itself: no division in the loop)
+    auto step_group = [&](int s) { return G == 1 ? 0 : s / nks; };
+    auto step_ks = [&](int s) { return G == 1 ? s : s % nks; };
 
     const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 32 * G : blockIdx.x * 64 * G;
     const int grows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 : 64;  // row offset between this block's groups
@@ -1779,7 +1783,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
         // the codes of step j (8 copies)
         auto issue = [&](int j) __attribute__((always_inline)) {
             const int s = wave + 4 * j;
-            const int gi = s / nks, ks = ks0 + s % nks;
+            const int gi = step_group(s), ks = ks0 + step_ks(s);
             const unsigned st = ring_lds0 + (unsigned)((j % KD) * kStage);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             const char* wsrc = wexp + (size_t)gi * grows * rowb + (size_t)ks * kRingSB;
@@ -1789,7 +1793,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
         // the group scales of step j (one copy)
         auto issue_scales = [&](int j) __attribute__((always_inline)) {
             const int s = wave + 4 * j;
-            const int gi = s / nks, ks = ks0 + s % nks;
+            const int gi = step_group(s), ks = ks0 + step_ks(s);
             const unsigned st = ring_lds0 + (unsigned)((j % KD) * kStage);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             lds_dma16_at(sexp + (size_t)(2 * ks + skg) * N + srow + gi * grows, st + kScaleOff);
@@ -1798,7 +1802,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
         // tile (values 128 kg + 32 lg + 8 q .. + 7 of the step, kg = 0..1,
         // q = 0..3)
         auto tload = [&](uint4 (&b)[NT][8], int j, auto lt_tag) __attribute__((always_inline)) {
-            const int ks = ks0 + (wave + 4 * j) % nks;
+            const int ks = ks0 + step_ks(wave + 4 * j);
 #pragma unroll
             for (int c = 0; c < decltype(lt_tag)::value; ++c) {
                 const char* src = trow[c] + (size_t)ks * (2 * 2 * kRingSB);
@@ -1831,7 +1835,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
             tload(tn, min(j + 1, nw - 1), lt_tag);
             const char* st = ring + (j % KD) * kStage;
             const float* sc = reinterpret_cast<const float*>(st + kScaleOff);
-            const int gi = (wave + 4 * j) / nks;
+            const int gi = step_group(wave + 4 * j);
             const int sw = (lr >> 1) & 7;
             // the compiler can overlap one tile's AND-ORs with the MFMAs of
             // another and interleave the LT tiles' MFMA chains (each MFMA's
