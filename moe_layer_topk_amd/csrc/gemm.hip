@@ -1738,9 +1738,12 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
     const int total = G * nks;
     const int nw = total > wave ? (total - wave + 3) / 4 : 0;
     // step s of the workgroup: row group s / nks, K step s % nks (with one
-    // group, s itself: no division in the loop)
+    // group, s itself: no division in the loop).  A wave with no steps
+    // still loads token values once (step index 0, so s = wave may be past
+    // the workgroup's steps): with one group that s maps to step 0, which
+    // every workgroup has, so the load stays inside the token rows
     auto step_group = [&](int s) { return G == 1 ? 0 : s / nks; };
-    auto step_ks = [&](int s) { return G == 1 ? s : s % nks; };
+    auto step_ks = [&](int s) { return G == 1 ? (s < nks ? s : 0) : s % nks; };
 
     const int n0 = (KIND == MOE_GEMM_GATE_UP_SILU) ? blockIdx.x * 32 * G : blockIdx.x * 64 * G;
     const int grows = (KIND == MOE_GEMM_GATE_UP_SILU) ? 32 : 64;  // row offset between this block's groups
