@@ -141,7 +141,52 @@ struct GemmArgs {
     int ksplit;    // decode DOWN only: K ranges handled by blockIdx.z
     float* cpart;  // non-null: DOWN writes float32 partials [ksplit][P][N] here instead of c
     int act_q8;    // fp8 DOWN: a holds e4m3 codes already quantised with amax/448
+    // one token routed by every workgroup of a decode kernel itself (the
+    // alignment buffers are then not read); NULL: the alignment gives the rows
+    const float* route_logits;  // [route_E] logits of the token
+    int route_E, route_renorm;
+    int32_t* route_ids;  // non-null: workgroup 0 writes the token's topk ids and weights
+    float* route_wts;
 };
+
+// The rows of active-expert slot `slot` of a decode kernel: the expert, its
+// pair-row count and where their pair ids start in `sorted`.  With
+// self-routing (one token) every wavefront routes the token as the route
+// kernel does; the slot's expert is the slot-th smallest of the selected
+// (distinct) ids and its one pair id the slot j it was selected in, and
+// workgroup 0 writes the token's ids and weights.  False for a slot past the
+// active experts.
+struct SlotRows {
+    int e, cnt, base, p1;
+};
+__device__ __forceinline__ bool slot_rows(const GemmArgs& g, int slot, SlotRows& r) {
+    if (g.route_logits) {
+        int sel;
+        float w;
+        route_token(g.route_logits, g.route_E, g.topk, g.route_renorm, &sel, &w);
+        const int lane = __lane_id();
+        int rank = 0;
+        for (int i = 0; i < g.topk; ++i) rank += (__shfl(sel, i, 64) < sel) ? 1 : 0;
+        const uint64_t m = __ballot(lane < g.topk && rank == slot);
+        if (m == 0) return false;
+        const int j = (int)__builtin_ctzll(m);
+        r.e = __builtin_amdgcn_readfirstlane(__shfl(sel, j, 64));
+        r.cnt = 1;
+        r.base = 0;
+        r.p1 = j;  // pair id t * topk + j of token 0
+        if (g.route_ids && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && (int)threadIdx.x < g.topk) {
+            g.route_ids[threadIdx.x] = sel;
+            g.route_wts[threadIdx.x] = w;
+        }
+        return true;
+    }
+    if (slot >= *g.num_active) return false;
+    r.e = g.active[slot];
+    r.cnt = g.counts[r.e];
+    r.base = g.offsets[r.e];
+    r.p1 = 0;
+    return true;
+}
 
 __device__ __forceinline__ void amax_publish(float m, float* dst) {
 #pragma unroll
@@ -1078,10 +1123,12 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
     extern __shared__ __attribute__((aligned(1024))) char ring_lds[];
 
     const int slot = blockIdx.y;
-    if (slot >= *g.num_active) return;
-    const int e = g.active[slot];
-    const int cnt = g.counts[e];
-    const int base = g.offsets[e];
+    SlotRows sr;
+    if (!slot_rows(g, slot, sr)) return;
+    const int e = sr.e;
+    const int cnt = sr.cnt;
+    // pair id of the expert's row r
+    auto pair_id = [&](int r) { return g.route_logits ? sr.p1 : g.sorted[sr.base + r]; };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1135,7 +1182,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
         size_t toff[NT][2];
         const char* trow = nullptr;  // TQ: this lane's float32 token row, at its lane group's 64 bytes
         if constexpr (TQ) {
-            const int p = g.sorted[base + min(pass + lr, cnt - 1)];
+            const int p = pair_id(min(pass + lr, cnt - 1));
             trow = reinterpret_cast<const char*>(g.a) + (size_t)p * K * 4 + 64 * lg;
         } else {
 #pragma unroll
@@ -1144,7 +1191,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
                 for (int h = 0; h < 2; ++h) {
                     const int rr = 16 * c + 8 * h + drow;
                     const int r = min(pass + rr, cnt - 1);
-                    const int p = g.sorted[base + r];
+                    const int p = pair_id(r);
                     const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
                     toff[c][h] = (size_t)src * rowb + ring_swz(dpc, rr) * 16;
                 }
@@ -1319,7 +1366,7 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
             const int gi = gq / kPer, q = gq % kPer;
             const int r = pass + c * 16 + lr;
             if (r >= cnt) continue;
-            const int p = g.sorted[base + r];
+            const int p = pair_id(r);
             if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
                 f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1721,10 +1768,12 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
     extern __shared__ __attribute__((aligned(1024))) char w4_lds[];
 
     const int slot = blockIdx.y;
-    if (slot >= *g.num_active) return;
-    const int e = g.active[slot];
-    const int cnt = g.counts[e];
-    const int base = g.offsets[e];
+    SlotRows sr;
+    if (!slot_rows(g, slot, sr)) return;
+    const int e = sr.e;
+    const int cnt = sr.cnt;
+    // pair id of the expert's row r
+    auto pair_id = [&](int r) { return g.route_logits ? sr.p1 : g.sorted[sr.base + r]; };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1779,7 +1828,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
         const char* trow[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-            const int p = g.sorted[base + min(pass + 16 * c + lr, cnt - 1)];
+            const int p = pair_id(min(pass + 16 * c + lr, cnt - 1));
             const int src = (KIND == MOE_GEMM_GATE_UP_SILU) ? p / g.topk : p;
             trow[c] = reinterpret_cast<const char*>(g.a) + (size_t)src * K * 2 + 64 * lg;
         }
@@ -1935,7 +1984,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) gemm_decode_w4_kernel(GemmArgs
             const int gi = gq / kPer, q = gq % kPer;
             const int r = pass + c * 16 + lr;
             if (r >= cnt) continue;
-            const int p = g.sorted[base + r];
+            const int p = pair_id(r);
             if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
                 f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -2248,7 +2297,12 @@ static hipError_t launch_kind(const GemmCall& c, const GemmArgs& a, int64_t cap,
 
 hipError_t launch_grouped_gemm(const GemmCall& c, hipStream_t s) {
     if (c.M == 0) return hipSuccess;
-    GemmArgs a;
+    // self-routing is implemented by the bf16 and int4 decode kernels only,
+    // for one token; any other kernel would read an alignment nobody wrote
+    if (c.route_logits && (c.M != 1 || !(c.dtype == MOE_BF16 || c.dtype == MOE_W4A16) ||
+                           choose_gemm_path(c) != GemmPath::kDecode))
+        return hipErrorInvalidValue;
+    GemmArgs a{};
     a.a = c.a;
     a.a_scale = c.a_scale;
     a.w = c.w;
@@ -2268,6 +2322,11 @@ hipError_t launch_grouped_gemm(const GemmCall& c, hipStream_t s) {
     a.ksplit = c.ksplit;
     a.cpart = c.cpart;
     a.act_q8 = c.act_q8 ? 1 : 0;
+    a.route_logits = c.route_logits;
+    a.route_E = c.E;
+    a.route_renorm = c.route_renorm;
+    a.route_ids = c.route_ids;
+    a.route_wts = c.route_wts;
     const int64_t cap = moe_align_capacity(c.M, c.topk, c.E, c.block_m);
     if (c.kind == MOE_GEMM_GATE_UP_SILU) return launch_kind<MOE_GEMM_GATE_UP_SILU>(c, a, cap, s);
     return launch_kind<MOE_GEMM_DOWN>(c, a, cap, s);

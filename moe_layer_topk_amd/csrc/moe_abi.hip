@@ -239,11 +239,18 @@ moe_status check_fused(moe_dtype dtype, const void* x, const float* x_scale, con
 // weights w1/w2 hold, in that order) and wts the routing weights.
 moe_status run_experts(moe_dtype dtype, const void* x, const float* x_scale, const void* w1, const float* w1_scale,
                        const void* w2, const float* w2_scale, int32_t M, int32_t E, int32_t topk, int32_t H,
-                       int32_t I, void* out, const float* wts, const FusedLayout& L, hipStream_t s) {
+                       int32_t I, void* out, const float* wts, const FusedLayout& L, hipStream_t s,
+                       const float* route_logits, int32_t renormalize, int32_t* route_ids) {
     const bool fp8 = dtype == MOE_FP8_E4M3;
     const moe_dtype inter = dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
     GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, x, x_scale, w1, w1_scale, L.al, M, topk, E, 2 * I, H,
                 L.block_m, L.act, fp8 ? L.amax : nullptr};
+    // route_logits: the GEMMs route the one token themselves; the gate/up
+    // launch writes its ids and weights (which the combine reads)
+    g1.route_logits = route_logits;
+    g1.route_renorm = renormalize;
+    g1.route_ids = route_ids;
+    g1.route_wts = const_cast<float*>(wts);
     if (launch_grouped_gemm(g1, s) != hipSuccess) return MOE_ERR_HIP;
     // e4m3: the down kernel quantises the float32 intermediate as it loads it,
     // or (tile kernels) reads codes quantised once here
@@ -251,10 +258,25 @@ moe_status run_experts(moe_dtype dtype, const void* x, const float* x_scale, con
     if (codes && launch_quant_act(L.act, L.amax, L.act_q, (size_t)M * topk * I, s) != hipSuccess) return MOE_ERR_HIP;
     GemmCall g2{MOE_GEMM_DOWN, dtype, codes ? L.act_q : L.act, fp8 ? L.amax : nullptr, w2, w2_scale, L.al, M, topk, E,
                 H, I, L.block_m, L.y, nullptr, L.ksplit, L.ypart, codes};
+    g2.route_logits = route_logits;
+    g2.route_renorm = renormalize;
     if (L.dc) return hip_status(launch_down_combine(g2, wts, out, s));  // y stays on chip
     if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
     if (L.ksplit > 1) return hip_status(launch_combine_partials(L.ypart, L.ksplit, wts, M, topk, H, inter, out, s));
     return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));
+}
+
+// One token of a bf16 or int4 layer whose GEMMs both run the decode kernels
+// (the kernels that can route a token themselves) and whose down GEMM is not
+// the fused down + combine kernel (it reads the alignment).
+static bool self_route_fits(moe_dtype dtype, int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I,
+                            const FusedLayout& L) {
+    if (M != 1 || L.dc || !(dtype == MOE_BF16 || dtype == MOE_W4A16)) return false;
+    const GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, nullptr, nullptr, nullptr, nullptr, {}, M, topk, E, 2 * I, H,
+                      L.block_m, nullptr, nullptr};
+    const GemmCall g2{MOE_GEMM_DOWN, dtype, nullptr, nullptr, nullptr, nullptr, {}, M, topk, E, H, I,
+                      L.block_m, nullptr, nullptr};
+    return choose_gemm_path(g1) == GemmPath::kDecode && choose_gemm_path(g2) == GemmPath::kDecode;
 }
 
 // The launch sequence over a carved workspace (arguments already checked, M > 0).
@@ -270,6 +292,13 @@ moe_status run_fused(moe_dtype dtype, const void* x, const float* x_scale, const
     float* wts = topk_weights_out ? topk_weights_out : L.wts;
     float* logits = const_cast<float*>(router_logits);
     const moe_dtype xdt = dtype == MOE_W4A16 ? MOE_BF16 : dtype;  // the activations' storage
+    if (!router_w && self_route_fits(dtype, M, E, topk, H, I, L)) {
+        // one token on the decode kernels: they route it themselves, so the
+        // layer needs no route / align launch (the launch and its dependent
+        // loads are most of the non-GEMM time at one token)
+        return run_experts(dtype, x, x_scale, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, out, wts, L, s,
+                           router_logits, renormalize, ids);
+    }
     if (router_w && router_route_align_fits(M, E, H)) {
         // router scores, top-k and alignment in one launch
         if (launch_router_route_align(xdt, x, x_scale, router_w, H, logits, M, E, topk, renormalize, ids, wts,

@@ -46,6 +46,7 @@ moe_status check_fused(moe_dtype dtype, const void* x, const float* x_scale, con
 // that w1/w2 hold and wts holds the routing weights.
 moe_status run_experts(moe_dtype dtype, const void* x, const float* x_scale, const void* w1, const float* w1_scale,
                        const void* w2, const float* w2_scale, int32_t M, int32_t E, int32_t topk, int32_t H,
-                       int32_t I, void* out, const float* wts, const FusedLayout& L, hipStream_t s);
+                       int32_t I, void* out, const float* wts, const FusedLayout& L, hipStream_t s,
+                       const float* route_logits = nullptr, int32_t renormalize = 1, int32_t* route_ids = nullptr);
 
 }  // namespace moe

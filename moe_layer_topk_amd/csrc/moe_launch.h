@@ -56,6 +56,14 @@ struct GemmCall {
     int ksplit = 1;         // decode DOWN: split of K across workgroups
     float* cpart = nullptr;  // with ksplit > 1: float32 partials [ksplit][P][N] instead of c
     bool act_q8 = false;     // fp8 DOWN: a holds e4m3 codes (quantised with amax/448), not the float32 act
+    // self-routing (M = 1, bf16 or W4A16 decode kernels): every workgroup
+    // routes the token from its logits instead of reading the alignment (al
+    // is then unused); route_ids / route_wts, when set, receive its topk ids
+    // and weights (written by one workgroup)
+    const float* route_logits = nullptr;
+    int route_renorm = 1;
+    int32_t* route_ids = nullptr;
+    float* route_wts = nullptr;
 };
 
 // Kernel family chosen for a call (decode for few rows per expert, or when
