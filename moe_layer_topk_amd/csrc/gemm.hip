@@ -778,9 +778,9 @@ struct P2Mfma {
 // rationed for occupancy.  A stage holds C::RowBytes bytes of every row
 // (64 bf16 or 128 e4m3 values of K).
 // NTW: weight tiles are copied with the non-temporal hint (chosen at launch
-// when each weight tile feeds at most two row tiles, so L2 reuse of the
-// weights is small; measured on the e4m3 512-token layer: 5% faster, on the
-// 4096-token Mixtral layer, where weight tiles are reused, 10% slower).
+// when each weight tile feeds about one row tile, so L2 reuse of the weights
+// is small; measured on the e4m3 512-token layer: 5% faster, on the layers
+// whose experts hold more rows, where weight tiles are reused, 7-10% slower).
 template <int KIND, int DT, class C, bool NTW>
 __global__ void __launch_bounds__(C::Threads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
@@ -1030,7 +1030,7 @@ using PrefillCfg64 = P2Cfg<64, 256, 64, 3>;
 static_assert(PrefillCfg::BN == PrefillCfg64::BN, "one weight-tile width");
 
 template <int KIND, int DT, class C, bool NTW>
-static hipError_t launch_prefill2_nt(const GemmArgs& a, int64_t cap, hipStream_t s) {
+static hipError_t launch_prefill2_nt(const GemmArgs& a, int64_t cap, int E, hipStream_t s) {
     const int m_tiles = (int)(cap / C::BM);
     const int n_tiles = (KIND == MOE_GEMM_GATE_UP_SILU) ? (a.N / 2) / (C::BN / 2) : a.N / C::BN;
     const int nb = m_tiles * n_tiles;
@@ -1040,21 +1040,31 @@ static hipError_t launch_prefill2_nt(const GemmArgs& a, int64_t cap, hipStream_t
         reinterpret_cast<const void*>(&gemm_prefill2_kernel<KIND, DT, C, NTW>), hipFuncAttributeMaxDynamicSharedMemorySize,
         C::LdsBytes);
     if (attr != hipSuccess) return attr;
-    // weight tiles per group: all of them when there are few (each token tile
-    // is then fetched once per XCD), else 2 (measured over the Mixtral, e4m3
-    // and 128-expert layers: 2 matches 4 on the first and is 7% faster on the
-    // e4m3 one, whose row tiles mostly belong to different experts)
-    const int group_n = n_tiles <= 8 ? n_tiles : 2;
+    // weight tiles per group.  DOWN: one (the row tiles of a weight tile run
+    // back to back; measured down GEMM times, one tile against the rule
+    // below: Mixtral 4096 tokens 1043 -> 1015 us, e4m3 512 tokens 480 -> 429,
+    // 128 experts at 2048 tokens 148 -> 126).  GATE_UP: one as well when an
+    // expert averages at most 64 pairs (one row tile each: e4m3 512 tokens
+    // 894 -> 852 us); otherwise all of them when there are few (each token
+    // tile is then fetched once per XCD), else 2 (Mixtral 4096 tokens: 2
+    // against 1, 3, 4, 8, 16: 1954 against 2024, 1974, 2020, 2100, 2330 us;
+    // 128 experts at 2048 tokens: all six 244 us, one 257)
+    const bool one = KIND == MOE_GEMM_DOWN || (long)a.P <= 64L * E;
+    const int group_n = one ? 1 : (n_tiles <= 8 ? n_tiles : 2);
     hipLaunchKernelGGL((gemm_prefill2_kernel<KIND, DT, C, NTW>), dim3(grid), dim3(C::Threads), C::LdsBytes, s, a, m_tiles,
                        n_tiles, group_n);
     return hipGetLastError();
 }
 
-// rows per expert (P / E) at most 256: the weights go non-temporal
+// pairs per expert (P / E) at most 64: each weight tile feeds about one row
+// tile, and the weights go non-temporal (e4m3 512 tokens, P / E = 64: 1.48
+// against 1.40 ms cached); with more, an expert's second row tile re-reads
+// its weight tiles from L2 (128 experts at 2048 tokens, P / E = 128: cached
+// 0.426 against 0.457 ms non-temporal)
 template <int KIND, int DT, class C>
 static hipError_t launch_prefill2(const GemmArgs& a, int64_t cap, int E, hipStream_t s) {
-    if ((long)a.P <= 256L * E) return launch_prefill2_nt<KIND, DT, C, true>(a, cap, s);
-    return launch_prefill2_nt<KIND, DT, C, false>(a, cap, s);
+    if ((long)a.P <= 64L * E) return launch_prefill2_nt<KIND, DT, C, true>(a, cap, E, s);
+    return launch_prefill2_nt<KIND, DT, C, false>(a, cap, E, s);
 }
 
 // ------------------------------------------------------ decode (LDS ring)
