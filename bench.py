@@ -102,9 +102,9 @@ def fused_block_m(cfg, M):
     if cfg.dtype in ("f32", "w4a16"):
         return 16
     pe = (M * cfg.topk) // cfg.E
-    if pe > (32 if cfg.dtype == "fp8" else 64):
-        return 128
-    return 64 if cfg.dtype == "fp8" and M >= 2 else 16
+    if cfg.dtype == "fp8":
+        return 128 if pe > 32 else (64 if M >= 2 else 16)
+    return 128 if pe > 48 else (64 if pe > 24 else 16)
 
 
 def fp8_quantises_on_load(cfg, M):

@@ -2144,12 +2144,13 @@ GemmPath choose_gemm_path(const GemmCall& g) {
     if (env && strcmp(env, "prefill") == 0 && pre_ok) return GemmPath::kPrefill;
     const long P = (long)g.M * g.topk;
     const long per_expert = P / g.E;
-    // e4m3 products cost a quarter of bf16's per byte on the f8f6f4 MFMA, so
-    // the tile kernel (weights read once per row tile) wins from fewer pairs
-    // per expert than for bf16: from 32 on 128-row tiles, and on 64-row tiles
-    // at any batch (what the fused e4m3 layer asks for from two tokens up)
+    // the tile kernel (weights read once per row tile) above 24 pairs per
+    // expert for bf16; e4m3 products cost a quarter of bf16's per byte on the
+    // f8f6f4 MFMA, so e4m3 takes it on 64-row tiles at any batch (what the
+    // fused e4m3 layer asks for from two tokens up) and on 128-row tiles
+    // above 32 pairs per expert
     if (g.dtype == MOE_FP8_E4M3 && g.block_m == 64 && pre_ok) return GemmPath::kPrefill;
-    const long min_rows = (g.dtype == MOE_FP8_E4M3) ? 32 : 64;
+    const long min_rows = (g.dtype == MOE_FP8_E4M3) ? 32 : 24;
     return (per_expert > min_rows && pre_ok) ? GemmPath::kPrefill : GemmPath::kDecode;
 }
 

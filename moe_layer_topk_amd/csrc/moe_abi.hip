@@ -46,17 +46,21 @@ int32_t fused_block_m(moe_dtype dtype, int32_t M, int32_t E, int32_t topk) {
     const char* env = getenv("MOE_GEMM_PATH");
     if (env && strcmp(env, "prefill") == 0) return 64;
     if (env && strcmp(env, "decode") == 0) return 16;
-    // 128-row tiles above 64 pairs per expert (32 for e4m3, whose products
-    // are cheap); below that the decode kernels, except that an e4m3 batch
-    // of two tokens or more runs the tile kernel on 64-row tiles (64-expert
-    // e4m3 layer, layer times against the decode kernels: 2 tokens 0.268 ->
-    // 0.250 ms, 8 tokens 0.738 -> 0.717, 32 tokens 1.048 -> 1.011, 256
-    // tokens 1.432 -> 1.196; one token a tie; the bf16 layers 12-25% slower
-    // on 64-row tiles, and the e4m3 one at 512 tokens 14% slower than on
-    // 128-row tiles)
+    // Tile height from the pairs per expert (layer times, tile kernel against
+    // the decode kernels).  bf16: the decode kernels up to 24 (Mixtral shape
+    // at 24: 0.506 ms against 0.517 on 64-row tiles; 128 experts at 16 and
+    // 24 are 4% faster and 12% slower there), 64-row tiles above that
+    // (Mixtral shape at 32 and 40: 0.536 -> 0.529, 0.560 -> 0.543 ms; 128
+    // experts at 32 and 40: 0.318 -> 0.276, 0.346 -> 0.280), 128-row tiles
+    // above 48 (Mixtral shape at 64: 0.890 -> 0.593 ms, 0.695 on 64-row
+    // tiles; 128 experts at 48 a tie between the two heights, at 64 0.468
+    // -> 0.312).  e4m3 (products a quarter of bf16's cost per byte): 128-row
+    // tiles above 32, else 64-row tiles from two tokens up (64-expert
+    // layer: 2 tokens 0.268 -> 0.250 ms, 32 tokens 1.048 -> 1.011, 256
+    // tokens 1.432 -> 1.196; one token a tie, left to the decode kernels)
     const int64_t per_expert = (int64_t)M * topk / E;
-    if (per_expert > ((dtype == MOE_FP8_E4M3) ? 32 : 64)) return 128;
-    return (dtype == MOE_FP8_E4M3 && M >= 2) ? 64 : 16;
+    if (dtype == MOE_FP8_E4M3) return per_expert > 32 ? 128 : (M >= 2 ? 64 : 16);
+    return per_expert > 48 ? 128 : (per_expert > 24 ? 64 : 16);
 }
 
 struct Carve {

@@ -412,9 +412,12 @@ def test_paths_agree_eq2_identity(dev, monkeypatch):
     assert d <= 1e-2 * outs["decode"].abs().max().item()
 
 
-@pytest.mark.parametrize("E,k,H,I,M", [(16, 8, 512, 256, 200), (8, 2, 1024, 512, 700), (4, 1, 256, 128, 1000)])
+@pytest.mark.parametrize("E,k,H,I,M", [(16, 8, 512, 256, 200), (8, 2, 1024, 512, 700), (4, 1, 256, 128, 1000),
+                                        (128, 8, 512, 256, 400), (8, 2, 1024, 512, 160), (8, 2, 512, 256, 200)])
 def test_fused_prefill_shapes(dev, E, k, H, I, M):
-    """Shapes with more than 64 rows per expert take the LDS-ring prefill kernel."""
+    """bf16 shapes with more than 24 pairs per expert take the LDS-ring tile
+    kernel: 64-row tiles up to 48 pairs per expert (the 400- and 160-token
+    cases, 25 and 40 on average), 128-row tiles above."""
     cfg = replace(CONFIGS["finegrained_bf16"], E=E, topk=k, H=H, I=I, router="zipf")
     say(f"fused prefill E={E} k={k} H={H} I={I} M={M}")
     check_layer(cfg, M, dev, tokens=np.arange(0, M, 7))
