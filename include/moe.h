@@ -193,11 +193,12 @@ size_t fused_moe_workspace_size(moe_dtype dtype, int32_t M, int32_t E, int32_t t
                                 int32_t I);
 
 /* The whole layer: route -> align -> GATE_UP GEMM -> DOWN GEMM -> combine, all
- * on `stream`, no host synchronisation.  For one token of a bf16 or W4A16
- * layer on the decode kernels the two GEMM launches route the token
+ * on `stream`, no host synchronisation.  For one token of a bf16, e4m3 or
+ * W4A16 layer on the decode kernels the two GEMM launches route the token
  * themselves (the same top-k and weights, bit for bit) and no route / align
  * launch runs; topk_ids_out / topk_weights_out are then written by the
- * GATE_UP launch.
+ * GATE_UP launch (e4m3: the intermediate's amax goes from the GATE_UP launch
+ * to the DOWN launch as partial maxima in the workspace, the same value).
  *  x              device [M][H]: float32, bfloat16 (also for MOE_W4A16) or e4m3
  *                 (x_scale -> float32)
  *  router_logits  device float32 [M][E]

@@ -147,6 +147,12 @@ struct GemmArgs {
     int route_E, route_renorm;
     int32_t* route_ids;  // non-null: workgroup 0 writes the token's topk ids and weights
     float* route_wts;
+    // e4m3 self-routing: GATE_UP writes the intermediate's amax as partial
+    // maxima here (G floats per workgroup at slot * gridDim.x * G +
+    // blockIdx.x * G: its maximum, then zeros), DOWN reduces amax_nparts of
+    // them instead of reading a_scale
+    float* amax_parts;
+    int amax_nparts;
 };
 
 // The rows of active-expert slot `slot` of a decode kernel: the expert, its
@@ -192,6 +198,34 @@ __device__ __forceinline__ void amax_publish(float m, float* dst) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     if (__lane_id() == 0 && m > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(dst), __float_as_uint(m));
+}
+
+// The workgroup's maximum of m (four wavefronts) into dst[0] and zeros into
+// dst[1..n): plain stores, so the partials need no clearing between calls.
+// lds: four floats no wavefront reads or writes any more (every wavefront of
+// the workgroup calls this).
+__device__ __forceinline__ void amax_parts_publish(float m, float* dst, int n, float* lds) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const int wave = threadIdx.x >> 6;
+    if (__lane_id() == 0) lds[wave] = m;
+    __syncthreads();
+    if ((int)threadIdx.x < n) dst[threadIdx.x] = threadIdx.x == 0 ? fmaxf(fmaxf(lds[0], lds[1]), fmaxf(lds[2], lds[3])) : 0.0f;
+}
+
+// The intermediate's e4m3 scale amax/448 from n partial maxima (every
+// thread of the workgroup calls this; lds: four floats, free until the
+// closing barrier).
+__device__ __forceinline__ float act_scale_from_parts(const float* parts, int n, float* lds) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, parts[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (__lane_id() == 0) lds[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const float a = fmaxf(fmaxf(lds[0], lds[1]), fmaxf(lds[2], lds[3]));
+    __syncthreads();
+    return a > 0.0f ? a / 448.0f : 1.0f;
 }
 
 // ----------------------------------------------------------------- decode
@@ -1174,7 +1208,9 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
         if constexpr (KIND == MOE_GEMM_GATE_UP_SILU) {
             scale = g.a_scale[0] * g.w_scale[e];
         } else {
-            qs = act_scale_from_amax(g.a_scale);
+            // (the ring's LDS is not in use before the first copies below)
+            qs = g.amax_parts ? act_scale_from_parts(g.amax_parts, g.amax_nparts, reinterpret_cast<float*>(ring_lds))
+                              : act_scale_from_amax(g.a_scale);
             scale = qs * g.w_scale[e];
         }
     }
@@ -1417,7 +1453,15 @@ __global__ void __launch_bounds__(kDecThreads) gemm_decode_ring_kernel(GemmArgs 
         // the next pass refills the rings over the reduction area
         __syncthreads();
     }
-    if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) amax_publish(amax, g.c_amax);
+    if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) {
+        // (every copy has landed and every wavefront has passed the pass's
+        // closing barrier: the LDS is free)
+        if (g.amax_parts)
+            amax_parts_publish(amax, g.amax_parts + ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * G, G,
+                               reinterpret_cast<float*>(ring_lds));
+        else
+            amax_publish(amax, g.c_amax);
+    }
 }
 
 template <int KIND, int DT, int NT, int G, int KD, bool TQ = false>
@@ -2310,11 +2354,16 @@ static hipError_t launch_kind(const GemmCall& c, const GemmArgs& a, int64_t cap,
 
 hipError_t launch_grouped_gemm(const GemmCall& c, hipStream_t s) {
     if (c.M == 0) return hipSuccess;
-    // self-routing is implemented by the bf16 and int4 decode kernels only,
-    // for one token; any other kernel would read an alignment nobody wrote
-    if (c.route_logits && (c.M != 1 || !(c.dtype == MOE_BF16 || c.dtype == MOE_W4A16) ||
+    // self-routing is implemented by the bf16, e4m3 and int4 decode kernels
+    // only, for one token; any other kernel would read an alignment nobody
+    // wrote.  e4m3 also takes its intermediate's amax through partials (the
+    // DOWN launch quantises the float32 intermediate on load; a launch over
+    // codes would need the separately quantised ones)
+    const bool fp8_ok = c.dtype == MOE_FP8_E4M3 && c.amax_parts && !c.act_q8;
+    if (c.route_logits && (c.M != 1 || !(c.dtype == MOE_BF16 || c.dtype == MOE_W4A16 || fp8_ok) ||
                            choose_gemm_path(c) != GemmPath::kDecode))
         return hipErrorInvalidValue;
+    if (c.amax_parts && !(c.route_logits && c.dtype == MOE_FP8_E4M3)) return hipErrorInvalidValue;
     GemmArgs a{};
     a.a = c.a;
     a.a_scale = c.a_scale;
@@ -2340,6 +2389,8 @@ hipError_t launch_grouped_gemm(const GemmCall& c, hipStream_t s) {
     a.route_renorm = c.route_renorm;
     a.route_ids = c.route_ids;
     a.route_wts = c.route_wts;
+    a.amax_parts = c.amax_parts;
+    a.amax_nparts = c.amax_nparts;
     const int64_t cap = moe_align_capacity(c.M, c.topk, c.E, c.block_m);
     if (c.kind == MOE_GEMM_GATE_UP_SILU) return launch_kind<MOE_GEMM_GATE_UP_SILU>(c, a, cap, s);
     return launch_kind<MOE_GEMM_DOWN>(c, a, cap, s);

@@ -98,6 +98,10 @@ FusedLayout fused_layout(char* ws, moe_dtype dtype, int32_t M, int32_t E, int32_
     L.act_q = (dtype == MOE_FP8_E4M3 && !L.q_on_load) ? c.take<char>((size_t)P * I) : nullptr;
     L.ksplit = L.dc ? 1 : down_ksplit(dtype, M, topk, E, H, I, L.block_m);
     L.ypart = L.ksplit > 1 ? c.take<float>((size_t)L.ksplit * P * H) : nullptr;
+    // one e4m3 token (the GEMMs may route it themselves): the intermediate's
+    // amax as partials, one per 32 gate/up output columns of each slot
+    L.amax_nparts = (dtype == MOE_FP8_E4M3 && M == 1) ? (P < E ? (int32_t)P : E) * (I / 32) : 0;
+    L.amax_parts = L.amax_nparts ? c.take<float>((size_t)L.amax_nparts) : nullptr;
     L.bytes = c.off;
     return L;
 }
@@ -262,6 +266,10 @@ moe_status run_experts(moe_dtype dtype, const void* x, const float* x_scale, con
     g1.route_renorm = renormalize;
     g1.route_ids = route_ids;
     g1.route_wts = const_cast<float*>(wts);
+    // e4m3 then passes the intermediate's amax through partials (nothing
+    // clears c_amax without the align launch)
+    float* parts = (fp8 && route_logits) ? L.amax_parts : nullptr;
+    g1.amax_parts = parts;
     if (launch_grouped_gemm(g1, s) != hipSuccess) return MOE_ERR_HIP;
     // e4m3: the down kernel quantises the float32 intermediate as it loads it,
     // or (tile kernels) reads codes quantised once here
@@ -271,18 +279,22 @@ moe_status run_experts(moe_dtype dtype, const void* x, const float* x_scale, con
                 H, I, L.block_m, L.y, nullptr, L.ksplit, L.ypart, codes};
     g2.route_logits = route_logits;
     g2.route_renorm = renormalize;
+    g2.amax_parts = parts;
+    g2.amax_nparts = parts ? L.amax_nparts : 0;
     if (L.dc) return hip_status(launch_down_combine(g2, wts, out, s));  // y stays on chip
     if (launch_grouped_gemm(g2, s) != hipSuccess) return MOE_ERR_HIP;
     if (L.ksplit > 1) return hip_status(launch_combine_partials(L.ypart, L.ksplit, wts, M, topk, H, inter, out, s));
     return hip_status(launch_combine(inter, L.y, wts, M, topk, H, inter, out, s));
 }
 
-// One token of a bf16 or int4 layer whose GEMMs both run the decode kernels
-// (the kernels that can route a token themselves) and whose down GEMM is not
-// the fused down + combine kernel (it reads the alignment).
+// One token of a bf16, e4m3 or int4 layer whose GEMMs both run the decode
+// kernels (the kernels that can route a token themselves) and whose down
+// GEMM is not the fused down + combine kernel (it reads the alignment); an
+// e4m3 down kernel must quantise the float32 intermediate on load.
 static bool self_route_fits(moe_dtype dtype, int32_t M, int32_t E, int32_t topk, int32_t H, int32_t I,
                             const FusedLayout& L) {
-    if (M != 1 || L.dc || !(dtype == MOE_BF16 || dtype == MOE_W4A16)) return false;
+    const bool fp8 = dtype == MOE_FP8_E4M3 && L.q_on_load && L.amax_parts;
+    if (M != 1 || L.dc || !(dtype == MOE_BF16 || dtype == MOE_W4A16 || fp8)) return false;
     const GemmCall g1{MOE_GEMM_GATE_UP_SILU, dtype, nullptr, nullptr, nullptr, nullptr, {}, M, topk, E, 2 * I, H,
                       L.block_m, nullptr, nullptr};
     const GemmCall g2{MOE_GEMM_DOWN, dtype, nullptr, nullptr, nullptr, nullptr, {}, M, topk, E, H, I,

@@ -27,6 +27,8 @@ struct FusedLayout {
     void* act_q;     // fp8 otherwise: e4m3 codes of act
     float* ypart;
     float* amax;
+    float* amax_parts;  // e4m3, one token: partial maxima of act ([topk][I/32]), see GemmCall
+    int32_t amax_nparts;
 };
 
 // ws == nullptr: only the sizes (L.bytes).  E: the experts the weights hold.

@@ -56,14 +56,21 @@ struct GemmCall {
     int ksplit = 1;         // decode DOWN: split of K across workgroups
     float* cpart = nullptr;  // with ksplit > 1: float32 partials [ksplit][P][N] instead of c
     bool act_q8 = false;     // fp8 DOWN: a holds e4m3 codes (quantised with amax/448), not the float32 act
-    // self-routing (M = 1, bf16 or W4A16 decode kernels): every workgroup
-    // routes the token from its logits instead of reading the alignment (al
-    // is then unused); route_ids / route_wts, when set, receive its topk ids
-    // and weights (written by one workgroup)
+    // self-routing (M = 1, bf16, e4m3 or W4A16 decode kernels): every
+    // workgroup routes the token from its logits instead of reading the
+    // alignment (al is then unused); route_ids / route_wts, when set, receive
+    // its topk ids and weights (written by one workgroup)
     const float* route_logits = nullptr;
     int route_renorm = 1;
     int32_t* route_ids = nullptr;
     float* route_wts = nullptr;
+    // e4m3 with self-routing: the intermediate's amax as partial maxima, one
+    // float per 32 gate/up output columns of each slot ([slots][N/2/32]),
+    // every one written by the GATE_UP launch (so nothing needs clearing)
+    // and reduced by the DOWN launch (amax_nparts of them) instead of c_amax
+    // / a_scale
+    float* amax_parts = nullptr;
+    int amax_nparts = 0;
 };
 
 // Kernel family chosen for a call (decode for few rows per expert, or when
