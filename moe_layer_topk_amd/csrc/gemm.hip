@@ -1057,8 +1057,9 @@ gemm_prefill2_kernel(GemmArgs g, int m_tiles, int n_tiles, int group_n) {
     if constexpr (DT == MOE_FP8_E4M3 && KIND == MOE_GEMM_GATE_UP_SILU) amax_publish(amax, g.c_amax);
 }
 
-// block shapes of the LDS-ring prefill kernel: 128-row tiles (what the fused
-// layer uses), and 64-row tiles for callers that align with block_m = 64
+// block shapes of the LDS-ring prefill kernel: 128-row tiles, and 64-row
+// tiles (the fused layer takes them for bf16 batches of 25-48 pairs per
+// expert and for e4m3 batches of two tokens up to 32 pairs per expert)
 using PrefillCfg = P2Cfg<128, 256, 64, 3>;
 using PrefillCfg64 = P2Cfg<64, 256, 64, 3>;
 static_assert(PrefillCfg::BN == PrefillCfg64::BN, "one weight-tile width");
