@@ -230,7 +230,9 @@ moe_status fused_moe(moe_dtype dtype, const void* x, const float* x_scale, const
  * shuffling and expert compute as one batched GPU operation).  For a few
  * tokens and a small router (up to 16 tokens, 64 K router weights and 128 K
  * multiply-adds) scoring, top-k and alignment are one launch; otherwise
- * moe_router_logits runs first.  The scores are the same bits either way.
+ * moe_router_logits runs first, and for one token whose GEMMs route it
+ * themselves (as in fused_moe) it is the only launch before them.  The
+ * scores are the same bits either way.
  * Workspace, arguments and errors as for fused_moe (fused_moe_workspace_size
  * gives the workspace). */
 moe_status fused_moe_router(moe_dtype dtype, const void* x, const float* x_scale, const float* router_w,

@@ -315,10 +315,13 @@ moe_status run_fused(moe_dtype dtype, const void* x, const float* x_scale, const
     float* wts = topk_weights_out ? topk_weights_out : L.wts;
     float* logits = const_cast<float*>(router_logits);
     const moe_dtype xdt = dtype == MOE_W4A16 ? MOE_BF16 : dtype;  // the activations' storage
-    if (!router_w && self_route_fits(dtype, M, E, topk, H, I, L)) {
+    if (self_route_fits(dtype, M, E, topk, H, I, L)) {
         // one token on the decode kernels: they route it themselves, so the
         // layer needs no route / align launch (the launch and its dependent
-        // loads are most of the non-GEMM time at one token)
+        // loads are most of the non-GEMM time at one token); from hidden
+        // states, the router scores come first
+        if (router_w && launch_router_logits(xdt, x, x_scale, router_w, M, E, H, logits, s) != hipSuccess)
+            return MOE_ERR_HIP;
         return run_experts(dtype, x, x_scale, w1, w1_scale, w2, w2_scale, M, E, topk, H, I, out, wts, L, s,
                            router_logits, renormalize, ids);
     }

@@ -57,10 +57,13 @@ def test_router_logits(dev, dtype, M, E, H):
 
 
 # (base workload, shape overrides, M): one-launch router + route + align for
-# up to 16 tokens with at most 64 K router weights, two launches otherwise
+# up to 16 tokens with at most 64 K router weights, two launches otherwise;
+# one bf16 / e4m3 token: the router launch, then GEMMs that route the token
+# themselves
 LAYERS = [("mixtral_decode_bf16", {}, 1), ("mixtral_decode_bf16", {}, 16), ("mixtral_decode_bf16", {}, 64),
           ("finegrained_bf16", {"H": 512}, 4), ("finegrained_bf16", {}, 3), ("tiny_f32", {}, 16),
-          ("fp8_e4m3", {"E": 16, "I": 1024}, 8), ("mixtral_prefill_bf16", {"H": 1024, "I": 1024}, 700)]
+          ("fp8_e4m3", {"E": 16, "I": 1024}, 8), ("mixtral_prefill_bf16", {"H": 1024, "I": 1024}, 700),
+          ("finegrained_bf16", {}, 1), ("fp8_e4m3", {"E": 16, "I": 1024}, 1)]
 
 
 @pytest.mark.parametrize("name,shape,M", LAYERS)
