@@ -2269,8 +2269,17 @@ static hipError_t launch_decode_ntg(const GemmArgs& a, int nslots, hipStream_t s
     return launch_decode_ntga<KIND, DT, NT, G, false>(a, nslots, s);
 }
 
+// Fraction of the workgroup slots of whole dispatch rounds that `wgs`
+// workgroups of `lds` bytes each keep busy (LDS decides how many share a CU).
+static double round_fill(double wgs, int lds) {
+    const double slots = 256.0 * (160 * 1024 / lds);
+    const double rounds = __builtin_ceil(wgs / slots);
+    return rounds > 0 ? wgs / (rounds * slots) : 1.0;
+}
+
 template <int KIND, int DT, int NT>
-static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_est, hipStream_t s) {
+static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_est, double active_exp,
+                                   hipStream_t s) {
     // Two row groups per workgroup (twice the weight rows per token load):
     // measured on the Mixtral, 128-expert and e4m3 decode layers, the bf16
     // down GEMM gains from 256 workgroups up (Mixtral shape at 8 to 64 tokens:
@@ -2300,11 +2309,20 @@ static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_es
     if constexpr (KIND == MOE_GEMM_DOWN) {
         // a short K (at most eight 256-byte steps, two per wavefront) leaves
         // each workgroup little to stream against its fixed costs: four row
-        // groups (128-expert layer, K = 768: 2-3% faster at 16 and 256 tokens)
+        // groups, unless two fill the chip's dispatch rounds better.  The
+        // active experts are estimated for uniform top-k routing.  128-expert
+        // layer, K = 768: at 256 tokens (all experts active, 1024 four-group
+        // workgroups, whole rounds) four groups are fastest; at 16 tokens
+        // (about 82 active: 659 four-group workgroups on 512 slots) two are
+        // 4% faster for the layer (down GEMM 55 -> 49 us)
         const long steps = (long)a.K * Opnd<DT>::kElemBytes / kDecSpan;
         if constexpr (NT < 4) {
-            if (steps <= 8 && a.ksplit == 1 && ncols % 256 == 0 && (long)(ncols / 256) * active_est >= 256)
+            if (steps <= 8 && a.ksplit == 1 && ncols % 256 == 0 && (long)(ncols / 256) * active_est >= 256) {
+                const double fill4 = round_fill((ncols / 256) * active_exp, DecRing<NT, 4, 2, false>::Lds);
+                const double fill2 = round_fill((ncols / 128) * active_exp, DecRing<NT, 2, 2, false>::Lds);
+                if (fill2 > fill4 + 0.05) return launch_decode_ntg<KIND, DT, NT, 2>(a, nslots, s);
                 return launch_decode_ntg<KIND, DT, NT, 4>(a, nslots, s);
+            }
         }
     }
     if (two && a.ksplit == 1 && ncols % rows2 == 0) return launch_decode_ntg<KIND, DT, NT, 2>(a, nslots, s);
@@ -2325,9 +2343,11 @@ static hipError_t launch_decode(const GemmArgs& a, int M, int topk, int E, hipSt
     const int nslots = (int)(P < E ? P : E);
     const long active_est = nslots;
     const int nt = decode_token_tiles(M, topk, E);
-    if (nt == 1) return launch_decode_nt<KIND, DT, 1>(a, nslots, active_est, s);
-    if (nt == 2) return launch_decode_nt<KIND, DT, 2>(a, nslots, active_est, s);
-    return launch_decode_nt<KIND, DT, 4>(a, nslots, active_est, s);
+    // expected distinct experts among M tokens' top-k picks under uniform routing
+    const double active_exp = E * (1.0 - __builtin_pow(1.0 - (double)topk / E, (double)M));
+    if (nt == 1) return launch_decode_nt<KIND, DT, 1>(a, nslots, active_est, active_exp, s);
+    if (nt == 2) return launch_decode_nt<KIND, DT, 2>(a, nslots, active_est, active_exp, s);
+    return launch_decode_nt<KIND, DT, 4>(a, nslots, active_est, active_exp, s);
 }
 
 bool fp8_down_quantises_on_load(int M, int topk, int E, int N, int K, int block_m) {
