@@ -2296,14 +2296,17 @@ static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_es
         // four row groups per workgroup for the gate/up GEMM: always for
         // e4m3 (a row holds half the bytes of a bf16 one, so one group is few
         // copy steps; measured 1-4% faster on the 64-expert layer at 1, 8
-        // and 32 tokens), and for bf16 when the one-group
-        // grid is at most 1024 workgroups and the four-group one still at
-        // least 128, so the launch fits in one round (Mixtral shape at one
-        // token: 896 -> 224 workgroups, 7% faster; with larger grids four
-        // groups measured 2-3% slower)
+        // and 32 tokens), and for bf16 when the one-group grid is at most
+        // 1024 workgroups and the four-group one, over the experts expected
+        // to be active, still covers most CUs, so the launch fits in one
+        // round (Mixtral shape at one token: 896 -> 224 workgroups, 7%
+        // faster; with larger grids four groups measured 2-3% slower, and
+        // the 128-expert layer at 4 tokens, about 175 four-group
+        // workgroups, 5% slower than with one)
         const long g1 = (long)(ncols / 32) * active_est;
+        const double g4_exp = (ncols / 128) * active_exp;
         if (ncols % 128 == 0 && a.ksplit == 1 &&
-            (DT == MOE_FP8_E4M3 || (DT == MOE_BF16 && g1 <= 1024 && g1 / 4 >= 128)))
+            (DT == MOE_FP8_E4M3 || (DT == MOE_BF16 && g1 <= 1024 && g4_exp >= 224.0)))
             return launch_decode_ntg<KIND, DT, NT, 4>(a, nslots, s);
     }
     if constexpr (KIND == MOE_GEMM_DOWN) {
