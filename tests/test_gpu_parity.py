@@ -328,8 +328,12 @@ def check_layer(cfg, M, dev, tokens=None, act_amax=None, batch=None):
     return out
 
 
+# 128 experts at 3-6 tokens: batch sizes where the decode GEMMs' row-group
+# counts follow the active experts expected for the batch (one gate/up
+# group; two down groups at 3 and 4 tokens, four at 5 and 6)
 LAYER_CASES = [("tiny_f32", 16), ("mixtral_decode_bf16", 1), ("mixtral_decode_bf16", 8),
-               ("finegrained_bf16", 1), ("finegrained_bf16", 16), ("fp8_e4m3", 1), ("fp8_e4m3", 8)]
+               ("finegrained_bf16", 1), ("finegrained_bf16", 3), ("finegrained_bf16", 4), ("finegrained_bf16", 5),
+               ("finegrained_bf16", 6), ("finegrained_bf16", 16), ("fp8_e4m3", 1), ("fp8_e4m3", 8)]
 
 
 @pytest.mark.parametrize("name,M", LAYER_CASES)
