@@ -2286,12 +2286,17 @@ static hipError_t launch_decode_nt(const GemmArgs& a, int nslots, long active_es
     // 3-4% over one group), the gate/up GEMM only for bf16 with two token
     // tiles and at least 512 workgroups; the e4m3 down GEMM with one token
     // tile (token values quantised in registers) is as fast or faster with
-    // one (64-expert layer at 8 tokens: 246 -> 233 us)
+    // one (64-expert layer at 8 tokens: 246 -> 233 us).  With one token
+    // tile the bf16 gate/up GEMM takes two when a weight row is at least
+    // 8 KB (Mixtral shape at 2 tokens 3.5% faster for the layer, at 4-8
+    // tokens 0.4-0.6%; the 128-expert layer's 4 KB rows measured 1-2%
+    // slower with two)
     const int ncols = (KIND == MOE_GEMM_GATE_UP_SILU) ? a.N / 2 : a.N;
     const int rows2 = (KIND == MOE_GEMM_GATE_UP_SILU) ? 64 : 128;
     const bool two = (KIND == MOE_GEMM_DOWN)
                          ? (NT < 4 && !(DT == MOE_FP8_E4M3 && NT == 1) && (long)(ncols / rows2) * active_est >= 256)
-                         : (DT == MOE_BF16 && NT == 2 && (long)(ncols / rows2) * active_est >= 512);
+                         : (DT == MOE_BF16 && ((NT == 2 && (long)(ncols / rows2) * active_est >= 512) ||
+                                               (NT == 1 && 2L * a.K >= 8192)));
     if constexpr (KIND == MOE_GEMM_GATE_UP_SILU && NT < 4) {
         // four row groups per workgroup for the gate/up GEMM: always for
         // e4m3 (a row holds half the bytes of a bf16 one, so one group is few
